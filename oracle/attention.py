@@ -1,0 +1,195 @@
+"""Plain fp64 CPU oracle of exact scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the bench's
+CPU-baseline leg, never by the library or its Python binding.
+
+What it computes (the "standard attention" data flow of [P1] section 1 and
+the three steps of [P3] "Core idea"):
+
+    S = scale * Q K^T                     one N x N matrix per (batch, head)
+    S[i, j] = -inf for j > i              only when causal (reading below)
+    P = softmax(S) row by row             three passes: max, sum of exps, divide
+    O = P V
+    LSE[i] = m[i] + ln(l[i])              natural-log logsumexp of row i of S
+
+and, for training, the exact gradient of that definition (the pages give no
+backward formula, only that it recomputes from saved statistics: [P2] "Core
+mechanism", [P3] "A surprise"):
+
+    dV = P^T dO
+    dP = dO V^T
+    delta[i] = sum_j P[i, j] dP[i, j]     taken from the materialised P
+    dS = P * (dP - delta)                 softmax Jacobian applied row by row
+    dQ = scale * dS K
+    dK = scale * dS^T Q
+
+Readings where the pages leave a step open:
+  * Causal means a query sees keys at its own position and before it
+    (diagonal included); with equal query and key lengths no row is empty.
+    [P3] "Pitfalls", second pitfall.
+  * LSE is stored in natural log; the GPU may use log2 internally.
+  * Inputs arrive as fp64 arrays that already hold the values the GPU sees
+    (rounded to the run's dtype); every step here is fp64.
+
+Everything materialises S and P (in query-row chunks, whole rows at a time)
+so that a reader can check each line against the definition by eye. No
+blocking over keys, fusion or reordering happens here except in
+`attention_forward_online`, which exists to restate [P1] section 2's
+blockwise algorithm for the "online equals three-pass" invariant.
+"""
+
+import numpy as np
+
+# Query rows handled per chunk: bounds the materialised S/P to
+# ROW_CHUNK x N fp64 values per (batch, head) without changing any result
+# (each query row is computed on its own).
+ROW_CHUNK = 1024
+
+
+def _check(q, k, v):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, D] shape")
+    return q, k, v
+
+
+def _scores(q_rows, k_all, scale, row0, causal):
+    """S = scale * Q K^T for query rows row0.. of one head, masked if causal.
+
+    [P3] "Core idea", step 1; causal exclusion as read above.
+    """
+    s = scale * (q_rows @ k_all.T)
+    if causal:
+        n_rows, n_keys = s.shape
+        qi = row0 + np.arange(n_rows)[:, None]
+        kj = np.arange(n_keys)[None, :]
+        s = np.where(kj > qi, -np.inf, s)
+    return s
+
+
+def attention_probabilities(q, k, scale, causal):
+    """P = softmax(scale * Q K^T [+ causal mask]) for one head, three-pass.
+
+    The three passes of [P1] section 2's first paragraph: row max for
+    stability, sum of exponentials, then the division. q, k: [N, D].
+    Returns (P, m, l) with m the row max of S and l the row sum of exp(S - m).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    s = _scores(q, k, scale, 0, causal)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, m[:, 0], l[:, 0]
+
+
+def attention_forward(q, k, v, scale, causal):
+    """O and LSE of exact attention, materialising S and P (fp64).
+
+    q, k, v: [B, H, N, D]. Returns (O [B, H, N, D], LSE [B, H, N]).
+    [P1] section 1 (standard data flow), [P3] "Core idea" steps 1-3.
+    """
+    q, k, v = _check(q, k, v)
+    B, H, N, D = q.shape
+    o = np.empty((B, H, N, D), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, ROW_CHUNK):
+                r1 = min(N, r0 + ROW_CHUNK)
+                s = _scores(q[b, h, r0:r1], k[b, h], scale, r0, causal)
+                m = s.max(axis=1, keepdims=True)          # pass 1: row max
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)           # pass 2: sum of exps
+                p = e / l                                  # pass 3: divide
+                o[b, h, r0:r1] = p @ v[b, h]
+                lse[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def attention_forward_online(q, k, v, scale, causal, block):
+    """Blockwise online-softmax attention over key blocks (fp64).
+
+    Restates the algorithm of [P1] section 2: keep, per query row, a running
+    maximum (starting at -inf), a running sum (starting at 0) and an
+    unnormalised output (starting at 0). For each block of `block` keys:
+    scores of all queries against the block; new maximum = larger of the old
+    one and the block's row maximum; correction = exp(old max - new max);
+    block weights = exp(scores - new max); running sum = correction * sum +
+    row sum of the weights; output = correction * output + weights @ V_block.
+    After the last block the output is divided by the running sum. The
+    pages' sketch returns no LSE; here LSE = final max + ln(final sum).
+
+    A row whose maximum is still -inf (every key so far masked) has nothing
+    to correct: its correction is taken as 0 instead of exp(-inf + inf).
+    """
+    q, k, v = _check(q, k, v)
+    B, H, N, D = q.shape
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    o_out = np.empty((B, H, N, D), dtype=np.float64)
+    lse_out = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            run_max = np.full((N, 1), -np.inf)
+            run_sum = np.zeros((N, 1))
+            acc = np.zeros((N, D))
+            for j0 in range(0, N, block):
+                j1 = min(N, j0 + block)
+                s = scale * (q[b, h] @ k[b, h, j0:j1].T)
+                if causal:
+                    qi = np.arange(N)[:, None]
+                    kj = j0 + np.arange(j1 - j0)[None, :]
+                    s = np.where(kj > qi, -np.inf, s)
+                m_prev = run_max
+                m_curr = s.max(axis=1, keepdims=True)
+                run_max = np.maximum(m_prev, m_curr)
+                with np.errstate(invalid="ignore"):
+                    corr = np.where(np.isneginf(run_max), 0.0,
+                                    np.exp(m_prev - run_max))
+                    p = np.where(np.isneginf(run_max), 0.0,
+                                 np.exp(s - run_max))
+                run_sum = corr * run_sum + p.sum(axis=1, keepdims=True)
+                acc = corr * acc + p @ v[b, h, j0:j1]
+            o_out[b, h] = acc / run_sum
+            lse_out[b, h] = run_max[:, 0] + np.log(run_sum[:, 0])
+    return o_out, lse_out
+
+
+def attention_backward(q, k, v, do, scale, causal):
+    """dQ, dK, dV of exact attention for upstream gradient dO (fp64).
+
+    The exact gradient of attention_forward: P is materialised from its
+    definition (not from a saved LSE), then
+        dV = P^T dO, dP = dO V^T, delta = rowsum(P * dP),
+        dS = P * (dP - delta), dQ = scale * dS K, dK = scale * dS^T Q.
+    The pages only say the backward recomputes local blocks from saved
+    statistics ([P2] "Core mechanism"; [P3] "A surprise"); these formulas
+    are the chain rule through softmax, not taken from the pages.
+    """
+    q, k, v = _check(q, k, v)
+    do = np.asarray(do, dtype=np.float64)
+    if do.shape != q.shape:
+        raise ValueError("do must have q's shape")
+    B, H, N, D = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(q)
+    dv = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, ROW_CHUNK):
+                r1 = min(N, r0 + ROW_CHUNK)
+                s = _scores(q[b, h, r0:r1], k[b, h], scale, r0, causal)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                p = e / e.sum(axis=1, keepdims=True)
+                g = do[b, h, r0:r1]
+                dv[b, h] += p.T @ g
+                dp = g @ v[b, h].T
+                delta = (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - delta)
+                dq[b, h, r0:r1] = scale * (ds @ k[b, h])
+                dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])
+    return dq, dk, dv

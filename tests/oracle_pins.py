@@ -1,0 +1,320 @@
+"""Pins that tie the CPU oracle to facts fixed outside the oracle itself.
+
+Each pin takes an oracle module (normally `oracle.attention`; the mutation
+test hands in deliberately broken copies) and raises AssertionError when the
+oracle disagrees with:
+  * hand-derived exact examples (tests/golden/hand_examples.txt);
+  * closed forms (scale = 0, N = 1, constant V, causal row 0);
+  * invariants of the definition (rows of P sum to 1, permutations,
+    sum of dV equals sum of dO, columns of dK sum to zero);
+  * an independent scalar brute force over tiny inputs;
+  * torch's fp64 CPU scaled_dot_product_attention and autograd (library
+    routines for the same definition);
+  * central finite differences of the forward (for the backward).
+"""
+
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "hand_examples.txt")
+
+
+# ---------------------------------------------------------------- fixtures
+
+def _eval(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"ln": math.log}))  # noqa: S307
+
+
+def load_golden():
+    """Parse the hand-derived examples into {name: {key: ndarray}}."""
+    out, cur = {}, None
+    with open(GOLDEN) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            if line.startswith("[") and line.endswith("]"):
+                cur = line[1:-1]
+                out[cur] = {}
+                continue
+            key, expr = (s.strip() for s in line.split("=", 1))
+            rows = [[_eval(x) for x in r.split(",")] for r in expr.split(";")]
+            out[cur][key] = np.array(rows, dtype=np.float64)
+    return out
+
+
+def _as_bhnd(x):
+    """[N, D] -> [1, 1, N, D]."""
+    return np.asarray(x, dtype=np.float64)[None, None]
+
+
+def _rand(shape, seed, mult=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * mult
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_force(q, k, v, scale, causal):
+    """Scalar loops over one head; keys a query may see are enumerated
+    instead of masked. q, k, v: nested lists [N][D]."""
+    n, d = len(q), len(q[0])
+    o, lse = [], []
+    for i in range(n):
+        keys = list(range(i + 1)) if causal else list(range(n))
+        s = [scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        tot = sum(w)
+        o.append([sum(w[a] * v[j][t] for a, j in enumerate(keys)) / tot
+                  for t in range(d)])
+        lse.append(m + math.log(tot))
+    return o, lse
+
+
+# ---------------------------------------------------------------- forward pins
+
+def pin_golden_forward(orc):
+    for name, ex in load_golden().items():
+        q, k, v = (_as_bhnd(ex[x]) for x in ("q", "k", "v"))
+        scale = float(ex["scale"][0, 0])
+        for causal, tag in ((False, "full"), (True, "causal")):
+            o, lse = orc.attention_forward(q, k, v, scale, causal)
+            np.testing.assert_allclose(o[0, 0], ex["o_" + tag], atol=1e-14,
+                                       err_msg=f"golden {name} o_{tag}")
+            np.testing.assert_allclose(lse[0, 0], ex["lse_" + tag][:, 0], atol=1e-14,
+                                       err_msg=f"golden {name} lse_{tag}")
+
+
+def pin_brute_force(orc):
+    for seed, (n, d) in enumerate([(1, 1), (2, 3), (5, 4), (8, 2), (7, 3)]):
+        q, k, v = (_rand((1, 2, n, d), 100 + 3 * seed + t) for t in range(3))
+        scale = 0.7
+        for causal in (False, True):
+            o, lse = orc.attention_forward(q, k, v, scale, causal)
+            for h in range(2):
+                bo, bl = brute_force(q[0, h].tolist(), k[0, h].tolist(),
+                                     v[0, h].tolist(), scale, causal)
+                np.testing.assert_allclose(o[0, h], np.array(bo), atol=1e-13, rtol=0)
+                np.testing.assert_allclose(lse[0, h], np.array(bl), atol=1e-13, rtol=0)
+
+
+def pin_online_equals_three_pass(orc):
+    """[P1] section 2: the blockwise online result equals three-pass softmax."""
+    q, k, v = (_rand((1, 2, 150, 16), 7 + t) for t in range(3))
+    for causal in (False, True):
+        o3, l3 = orc.attention_forward(q, k, v, 0.25, causal)
+        for block in (1, 7, 128, 150, 1000):
+            oo, lo = orc.attention_forward_online(q, k, v, 0.25, causal, block)
+            np.testing.assert_allclose(oo, o3, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lo, l3, atol=1e-12, rtol=0)
+
+
+def pin_rows_sum_to_one(orc):
+    q, k = (_rand((33, 8), 11 + t) for t in range(2))
+    for causal in (False, True):
+        p, m, l = orc.attention_probabilities(q, k, 0.5, causal)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14, rtol=0)
+        if causal:
+            assert np.all(np.triu(p, 1) == 0.0)
+        s = 0.5 * q @ k.T
+        if causal:
+            s = np.where(np.triu(np.ones_like(s), 1) > 0, -np.inf, s)
+        np.testing.assert_allclose(m, s.max(axis=1), atol=0, rtol=0)
+
+
+def pin_constant_v(orc):
+    q, k = (_rand((2, 3, 40, 8), 21 + t) for t in range(2))
+    c = _rand((8,), 23)
+    v = np.broadcast_to(c, (2, 3, 40, 8)).copy()
+    for causal in (False, True):
+        o, _ = orc.attention_forward(q, k, v, 0.3, causal)
+        np.testing.assert_allclose(o, v, atol=1e-14, rtol=1e-14)
+
+
+def pin_causal_row0(orc):
+    q, k, v = (_rand((1, 2, 17, 5), 31 + t) for t in range(3))
+    o, lse = orc.attention_forward(q, k, v, 0.9, True)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.9 * (q[:, :, 0] * k[:, :, 0]).sum(-1),
+                               atol=1e-14, rtol=0)
+
+
+def pin_scale_zero(orc):
+    """scale = 0: uniform weights over the visible keys."""
+    n = 23
+    q, k, v = (_rand((1, 2, n, 6), 41 + t) for t in range(3))
+    o, lse = orc.attention_forward(q, k, v, 0.0, False)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape),
+                               atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse, np.log(n), atol=1e-14, rtol=0)
+    o, lse = orc.attention_forward(q, k, v, 0.0, True)
+    cum = np.cumsum(v, axis=2) / np.arange(1, n + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, cum, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(np.arange(1, n + 1)), lse.shape),
+                               atol=1e-14, rtol=0)
+
+
+def pin_single_key(orc):
+    """N = 1: the only weight is 1 and LSE is the single score."""
+    q, k, v = (_rand((2, 3, 1, 7), 51 + t) for t in range(3))
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 1.3, causal)
+        np.testing.assert_array_equal(o, v)
+        np.testing.assert_allclose(lse, 1.3 * (q * k).sum(-1)[..., 0][..., None],
+                                   atol=1e-14, rtol=0)
+
+
+def pin_permutations(orc):
+    """Non-causal: permuting keys with their values changes nothing;
+    permuting queries permutes the rows of O and LSE."""
+    q, k, v = (_rand((1, 1, 29, 8), 61 + t) for t in range(3))
+    o, lse = orc.attention_forward(q, k, v, 0.4, False)
+    perm = np.random.default_rng(5).permutation(29)
+    o2, lse2 = orc.attention_forward(q, k[:, :, perm], v[:, :, perm], 0.4, False)
+    np.testing.assert_allclose(o2, o, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse2, lse, atol=1e-14, rtol=0)
+    o3, lse3 = orc.attention_forward(q[:, :, perm], k, v, 0.4, False)
+    np.testing.assert_allclose(o3, o[:, :, perm], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse3, lse[:, :, perm], atol=1e-14, rtol=0)
+
+
+def pin_torch_sdpa(orc):
+    """torch's fp64 CPU scaled_dot_product_attention and logsumexp."""
+    q, k, v = (_rand((2, 3, 70, 16), 71 + t) for t in range(3))
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.21, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=causal, scale=0.21).numpy()
+        np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
+        s = 0.21 * (tq @ tk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(torch.ones(70, 70, dtype=torch.bool).triu(1), -math.inf)
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12, rtol=0)
+
+
+def pin_row_chunking(orc):
+    """Results do not depend on the row-chunk size used to bound memory."""
+    q, k, v = (_rand((1, 1, 37, 4), 81 + t) for t in range(3))
+    old = orc.ROW_CHUNK
+    try:
+        orc.ROW_CHUNK = 1024
+        o_a, l_a = orc.attention_forward(q, k, v, 0.5, True)
+        g_a = orc.attention_backward(q, k, v, v[:, :, ::-1].copy(), 0.5, True)
+        orc.ROW_CHUNK = 5
+        o_b, l_b = orc.attention_forward(q, k, v, 0.5, True)
+        g_b = orc.attention_backward(q, k, v, v[:, :, ::-1].copy(), 0.5, True)
+    finally:
+        orc.ROW_CHUNK = old
+    np.testing.assert_allclose(o_b, o_a, atol=1e-15, rtol=0)
+    np.testing.assert_allclose(l_b, l_a, atol=1e-15, rtol=0)
+    for a, b in zip(g_a, g_b):
+        np.testing.assert_allclose(b, a, atol=1e-14, rtol=0)
+
+
+# ---------------------------------------------------------------- backward pins
+
+def pin_golden_backward(orc):
+    ex = load_golden()
+    a = ex["A"]
+    dq, dk, dv = orc.attention_backward(*(_as_bhnd(a[x]) for x in ("q", "k", "v", "do")),
+                                        float(a["scale"][0, 0]), True)
+    np.testing.assert_allclose(dq[0, 0], a["dq_causal"], atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0], a["dk_causal"], atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0], a["dv_causal"], atol=1e-14)
+    b = ex["B"]
+    dq, dk, dv = orc.attention_backward(*(_as_bhnd(b[x]) for x in ("q", "k", "v", "do")),
+                                        float(b["scale"][0, 0]), False)
+    np.testing.assert_allclose(dq[0, 0], b["dq_full"], atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0], b["dk_full"], atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0], b["dv_full"], atol=1e-14)
+
+
+def pin_finite_differences(orc):
+    """Central differences of L = sum(O * dO) match dQ, dK, dV."""
+    h = 1e-6
+    for causal in (False, True):
+        q, k, v, do = (_rand((1, 2, 5, 3), 91 + t) for t in range(4))
+        grads = orc.attention_backward(q, k, v, do, 0.8, causal)
+        for which in range(3):
+            base = [q, k, v]
+            num = np.zeros_like(q)
+            it = np.nditer(q, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                lp = (orc.attention_forward(*plus, 0.8, causal)[0] * do).sum()
+                lm = (orc.attention_forward(*minus, 0.8, causal)[0] * do).sum()
+                num[idx] = (lp - lm) / (2 * h)
+            err = np.abs(grads[which] - num).max() / max(1.0, np.abs(num).max())
+            assert err < 1e-7, (causal, which, err)
+
+
+def pin_grad_sums(orc):
+    """sum_j dV_j = sum_i dO_i (rows of P sum to 1); sum_j dK_j = 0 (rows
+    of dS sum to 0)."""
+    q, k, v, do = (_rand((2, 2, 31, 6), 101 + t) for t in range(4))
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.6, causal)
+        np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12, rtol=0)
+
+
+def pin_constant_v_grads(orc):
+    q, k, do = (_rand((1, 2, 19, 4), 111 + t) for t in range(3))
+    v = np.broadcast_to(_rand((4,), 114), q.shape).copy()
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.6, causal)
+        np.testing.assert_allclose(dq, 0.0, atol=1e-13)
+        np.testing.assert_allclose(dk, 0.0, atol=1e-13)
+
+
+def pin_scale_zero_grads(orc):
+    """scale = 0, causal: dQ = dK = 0 and dV_j = sum_{i >= j} dO_i / (i + 1)."""
+    n = 13
+    q, k, v, do = (_rand((1, 2, n, 3), 121 + t) for t in range(4))
+    dq, dk, dv = orc.attention_backward(q, k, v, do, 0.0, True)
+    np.testing.assert_array_equal(dq, 0.0)
+    np.testing.assert_array_equal(dk, 0.0)
+    w = do / np.arange(1, n + 1)[None, None, :, None]
+    expect = np.flip(np.cumsum(np.flip(w, axis=2), axis=2), axis=2)
+    np.testing.assert_allclose(dv, expect, atol=1e-14, rtol=0)
+
+
+def pin_delta_two_ways(orc):
+    """rowsum(P * dP) equals rowsum(dO * O), the form a fused backward uses."""
+    q, k, v, do = (_rand((45, 8), 131 + t) for t in range(4))
+    for causal in (False, True):
+        p, _, _ = orc.attention_probabilities(q, k, 0.35, causal)
+        o, _ = orc.attention_forward(_as_bhnd(q), _as_bhnd(k), _as_bhnd(v), 0.35, causal)
+        a = (p * (do @ v.T)).sum(axis=1)
+        b = (do * o[0, 0]).sum(axis=1)
+        np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
+
+
+def pin_torch_autograd(orc):
+    q, k, v, do = (_rand((1, 2, 40, 8), 141 + t) for t in range(4))
+    for causal in (False, True):
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=causal, scale=0.45)
+        out.backward(torch.from_numpy(do))
+        got = orc.attention_backward(q, k, v, do, 0.45, causal)
+        for g, t in zip(got, (tq, tk, tv)):
+            np.testing.assert_allclose(g, t.grad.numpy(), atol=1e-12, rtol=0)
+
+
+FORWARD_PINS = [pin_golden_forward, pin_brute_force, pin_online_equals_three_pass,
+                pin_rows_sum_to_one, pin_constant_v, pin_causal_row0, pin_scale_zero,
+                pin_single_key, pin_permutations, pin_torch_sdpa, pin_row_chunking]
+BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_grad_sums,
+                 pin_constant_v_grads, pin_scale_zero_grads, pin_delta_two_ways,
+                 pin_torch_autograd]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -1,0 +1,75 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that the pins catch every one of them: a dropped term, a wrong sign, a wrong
+index or axis, a transposed or swapped operand."""
+
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "attention.py")
+
+MUTANTS = {
+    "mask_excludes_diagonal": ("s = np.where(kj > qi, -np.inf, s)\n    return s",
+                               "s = np.where(kj >= qi, -np.inf, s)\n    return s"),
+    "mask_wrong_side": ("s = np.where(kj > qi, -np.inf, s)\n    return s",
+                        "s = np.where(kj < qi, -np.inf, s)\n    return s"),
+    "mask_no_row_offset": ("qi = row0 + np.arange(n_rows)", "qi = np.arange(n_rows)"),
+    "scale_dropped": ("s = scale * (q_rows @ k_all.T)", "s = (q_rows @ k_all.T)"),
+    "lse_drops_max": ("lse[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])",
+                      "lse[b, h, r0:r1] = np.log(l[:, 0])"),
+    "lse_log2": ("lse[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])",
+                 "lse[b, h, r0:r1] = m[:, 0] + np.log2(l[:, 0])"),
+    "fwd_no_max_shift": ("                e = np.exp(s - m)\n                l = e.sum",
+                         "                e = np.exp(s)\n                l = e.sum"),
+    "fwd_sum_wrong_axis": ("l = e.sum(axis=1, keepdims=True)           # pass 2",
+                           "l = e.sum(axis=0, keepdims=True)           # pass 2"),
+    "fwd_values_reversed": ("o[b, h, r0:r1] = p @ v[b, h]",
+                            "o[b, h, r0:r1] = p @ v[b, h][::-1]"),
+    "fwd_values_are_keys": ("o[b, h, r0:r1] = p @ v[b, h]",
+                            "o[b, h, r0:r1] = p @ k[b, h]"),
+    "probs_no_normalise": ("return e / l, m[:, 0], l[:, 0]", "return e, m[:, 0], l[:, 0]"),
+    "online_no_out_correction": ("acc = corr * acc + p @ v[b, h, j0:j1]",
+                                 "acc = acc + p @ v[b, h, j0:j1]"),
+    "online_no_sum_correction": ("run_sum = corr * run_sum +", "run_sum = run_sum +"),
+    "online_corr_sign": ("np.exp(m_prev - run_max))", "np.exp(run_max - m_prev))"),
+    "bwd_dv_untransposed": ("dv[b, h] += p.T @ g", "dv[b, h] += p[:, :g.shape[0]] @ g"),
+    "bwd_dp_uses_keys": ("dp = g @ v[b, h].T", "dp = g @ k[b, h].T"),
+    "bwd_delta_dropped": ("ds = p * (dp - delta)", "ds = p * dp"),
+    "bwd_delta_sign": ("ds = p * (dp - delta)", "ds = p * (delta - dp)"),
+    "bwd_delta_axis": ("delta = (p * dp).sum(axis=1, keepdims=True)",
+                       "delta = (p * dp).sum(axis=1, keepdims=True) * 0 + (p * dp).mean()"),
+    "bwd_dq_no_scale": ("dq[b, h, r0:r1] = scale * (ds @ k[b, h])",
+                        "dq[b, h, r0:r1] = (ds @ k[b, h])"),
+    "bwd_dq_uses_values": ("dq[b, h, r0:r1] = scale * (ds @ k[b, h])",
+                           "dq[b, h, r0:r1] = scale * (ds @ v[b, h])"),
+    "bwd_dk_uses_grad": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
+                         "dk[b, h] += scale * (ds.T @ g)"),
+    "bwd_dk_sign": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
+                    "dk[b, h] -= scale * (ds.T @ q[b, h, r0:r1])"),
+}
+
+
+def _load_mutant(name, old, new):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutant {name}: pattern not found in oracle"
+    src = src.replace(old, new, 1)
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)  # noqa: S102
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(name, *MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # any failure means the pin caught it
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches the planted mistake '{name}'"
