@@ -1,0 +1,120 @@
+"""Fused exact attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libfa.so (include/fa.h): it checks tensors,
+allocates outputs with torch and passes raw device pointers and the current
+HIP stream to the C ABI. Every step of the computation runs in the HIP
+kernels; there is no fallback path.
+
+    o, lse = forward(q, k, v, causal=False, scale=None)
+    dq, dk, dv = backward(q, k, v, o, lse, do, causal=False, scale=None)
+    o = attention(q, k, v, causal=False, scale=None)   # autograd-aware
+
+Tensors are contiguous [B, H, N, D] of float32, float16 or bfloat16 on the
+GPU; the default scale is 1/sqrt(D).
+"""
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FaError  # noqa: F401
+
+_DTYPES = {torch.float32: _lib.FA_FP32, torch.float16: _lib.FA_FP16,
+           torch.bfloat16: _lib.FA_BF16}
+
+
+def _stream_handle(t):
+    """hipStream_t of torch's current stream on t's device (None = default)."""
+    return torch.cuda.current_stream(t.device).cuda_stream or None
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, D] shape, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"dtype must be float32, float16 or bfloat16 (all equal), got "
+                        f"{q.dtype}, {k.dtype}, {v.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)
+
+
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Fused forward. Returns (o, lse): o like q, lse fp32 [B, H, N] (natural log)."""
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, N, D, float(scale), int(bool(causal)),
+                            _DTYPES[q.dtype], _stream_handle(q))
+    _lib.check("fa_forward", st)
+    return out, lse
+
+
+def backward_workspace_bytes(B, H, N, D):
+    return int(_lib.load().fa_backward_workspace_bytes(B, H, N, D))
+
+
+def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
+    """Backward from the forward's o and lse. Returns (dq, dk, dv)."""
+    _check_qkv(q, k, v)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must match q (shape, dtype, device, contiguous)")
+    B, H, N, D = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    if scale is None:
+        scale = default_scale(D)
+    need = backward_workspace_bytes(B, H, N, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, D,
+                             float(scale), int(bool(causal)), _DTYPES[q.dtype],
+                             _stream_handle(q))
+    _lib.check("fa_backward", st)
+    return dq, dk, dv
+
+
+class _FlashAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = forward(q, k, v, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal=False, scale=None):
+    """Autograd-aware fused attention (O only)."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    return _FlashAttention.apply(q, k, v, causal, scale)

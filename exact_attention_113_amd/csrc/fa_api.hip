@@ -1,0 +1,161 @@
+// C ABI of libfa.so: argument validation, status reporting and dispatch to
+// the kernel launchers. Validation runs before any HIP call, so a rejected
+// call touches no device and writes nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+__attribute__((format(printf, 2, 3))) fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) != 0; }
+
+int64_t dtype_size(int dtype) {
+  switch (dtype) {
+    case FA_FP32: return 4;
+    case FA_FP16: return 2;
+    case FA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// Shape checks common to forward and backward. Returns FA_OK or the status
+// to report (with the error text set).
+fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t D, float scale, int dtype) {
+  if (B < 1) return fail(FA_ERR_INVALID_ARGUMENT, "B must be >= 1 (got %lld)", (long long)B);
+  if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1 (got %lld)", (long long)H);
+  if (N < 1) return fail(FA_ERR_INVALID_ARGUMENT, "N must be >= 1 (got %lld)", (long long)N);
+  if (D < 1) return fail(FA_ERR_INVALID_ARGUMENT, "D must be >= 1 (got %lld)", (long long)D);
+  if (dtype_size(dtype) == 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code %d", dtype);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  int64_t elems = 0, bytes = 0, rows = 0;
+  if (__builtin_mul_overflow(B, H, &rows) || __builtin_mul_overflow(rows, N, &rows) ||
+      __builtin_mul_overflow(rows, D, &elems) ||
+      __builtin_mul_overflow(elems, (int64_t)4, &bytes))
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*H*N*D overflows 64-bit byte offsets");
+  if (D != 64 && D != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
+  // Kernels index positions with 32-bit integers and launch one workgroup
+  // per 128 query rows of each (batch, head).
+  if (N > (int64_t)1 << 30)
+    return fail(FA_ERR_UNSUPPORTED, "sequence length %lld above 2^30", (long long)N);
+  const int64_t wgs = ((N + 127) / 128) * B * H;
+  if (wgs > (int64_t)0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "%lld workgroups exceed one grid", (long long)wgs);
+  return FA_OK;
+}
+
+fa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FA_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: HIP error %d (%s)", what, (int)e,
+           hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
+}  // namespace
+
+namespace fa {
+
+bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWorkspace* ws) {
+  if (B < 1 || H < 1 || N < 1 || D < 1) return false;
+  int64_t rows = 0, elems = 0, acc = 0, dl = 0;
+  if (__builtin_mul_overflow(B, H, &rows) || __builtin_mul_overflow(rows, N, &rows) ||
+      __builtin_mul_overflow(rows, D, &elems) || __builtin_mul_overflow(elems, (int64_t)4, &acc) ||
+      __builtin_mul_overflow(rows, (int64_t)4, &dl))
+    return false;
+  const int64_t round = 255;
+  if (acc > INT64_MAX - 2 * round - dl) return false;
+  ws->dq_acc_off = 0;
+  ws->dq_acc_bytes = (size_t)acc;
+  ws->delta_off = (size_t)((acc + round) & ~round);
+  ws->delta_bytes = (size_t)dl;
+  ws->total = ws->delta_off + (size_t)((dl + round) & ~round);
+  return true;
+}
+
+}  // namespace fa
+
+extern "C" {
+
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
+                     void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: q, k, v, o and lse must be non-NULL");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: q, k, v, o must be 16-byte aligned");
+  if (misaligned(lse, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: lse must be 4-byte aligned");
+  fa_status s = check_shape(B, H, N, D, scale, dtype);
+  if (s != FA_OK) return s;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, D, scale, causal, dtype, (hipStream_t)stream};
+  return hip_status(fa::launch_forward(a), "fa_forward");
+}
+
+size_t fa_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
+  fa::BwdWorkspace ws;
+  if (!fa::backward_workspace_layout(B, H, N, D, &ws)) return 0;
+  return ws.total;
+}
+
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                      int64_t D, float scale, int causal, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_backward: q, k, v, o, dout, lse, dq, dk, dv must be non-NULL");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_backward: tensors must be 16-byte aligned");
+  if (misaligned(lse, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_backward: lse must be 4-byte aligned");
+  fa_status s = check_shape(B, H, N, D, scale, dtype);
+  if (s != FA_OK) return s;
+  if (dtype == FA_FP32)
+    return fail(FA_ERR_UNSUPPORTED, "fa_backward: fp32 backward is not supported");
+  fa::BwdWorkspace ws;
+  if (!fa::backward_workspace_layout(B, H, N, D, &ws))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_backward: workspace size overflows");
+  if (!workspace)
+    return fail(FA_ERR_WORKSPACE, "fa_backward: workspace is NULL (needs %lld bytes)",
+                (long long)ws.total);
+  if (workspace_bytes < ws.total)
+    return fail(FA_ERR_WORKSPACE, "fa_backward: workspace too small (needs %lld bytes)",
+                (long long)ws.total);
+  if (misaligned(workspace, 256))
+    return fail(FA_ERR_WORKSPACE, "fa_backward: workspace must be 256-byte aligned");
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, D, scale, causal, dtype,
+                (hipStream_t)stream};
+  return hip_status(fa::launch_backward(a, ws), "fa_backward");
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

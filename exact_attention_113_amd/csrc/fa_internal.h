@@ -1,0 +1,53 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t B, H, N, D;
+  float scale;
+  int causal;
+  int dtype;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;
+  int64_t B, H, N, D;
+  float scale;
+  int causal;
+  int dtype;
+  hipStream_t stream;
+};
+
+// Byte offsets of the backward workspace's parts (each 256-byte aligned).
+struct BwdWorkspace {
+  size_t dq_acc_off, dq_acc_bytes;  // fp32 [B, H, N, D]
+  size_t delta_off, delta_bytes;    // fp32 [B, H, N]
+  size_t total;
+};
+bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWorkspace* ws);
+
+hipError_t launch_forward(const FwdArgs& a);
+hipError_t launch_backward(const BwdArgs& a, const BwdWorkspace& ws);
+
+}  // namespace fa

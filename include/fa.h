@@ -1,0 +1,155 @@
+/*
+ * fa.h - C ABI of the fused exact-attention library (libfa.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V
+ *
+ * in one fused, tiled pass with an online softmax: each query row keeps a
+ * running maximum, a running sum of exponentials and a rescaled output
+ * accumulator, and the N x N score and probability matrices never leave
+ * the chip. Sources, cited by page title and section:
+ *   - "From Self-Attention to FlashAttention" (wmrh.cn), section 1 (the
+ *     standard and flash data flows) and section 2 (online softmax);
+ *   - "Flash Attention algorithm design and I/O optimisation" interview
+ *     page (algomooc.com), "Positioning" (the result is exact up to
+ *     floating-point ordering) and "Core mechanism" (tiling, online
+ *     softmax, backward by recomputation from saved row statistics);
+ *   - "FlashAttention in ops-transformer" (mhpn.cn), "Core idea",
+ *     "Online softmax", "Complete operator" (causal and scale arguments,
+ *     workspace query, asynchronous launch on a caller stream),
+ *     "Pitfalls" (causal mask; fp32 softmax inside half-precision kernels)
+ *     and "A surprise" (the backward keeps forward state).
+ *
+ * Conventions shared by every entry point
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV are contiguous row-major
+ *              [B, H, N, D] tensors (batch, head, position, head dim) of the
+ *              call's dtype. LSE is contiguous fp32 [B, H, N].
+ *   Memory     Every tensor pointer is device memory owned by the caller,
+ *              16-byte aligned. The library never allocates, frees or
+ *              synchronises, and keeps no state between calls except the
+ *              per-thread error text of fa_last_error.
+ *   Stream     Work is enqueued on `stream` (a hipStream_t; NULL means the
+ *              default stream) and runs asynchronously; a returned FA_OK
+ *              means the launch was accepted.
+ *   Causal     A query at position i sees keys 0..i (diagonal included).
+ *   Scale      Any finite float; callers usually pass 1/sqrt(D).
+ *   Errors     Arguments are validated before any device work. A rejected
+ *              call returns a non-zero fa_status, writes nothing and sets
+ *              the text returned by fa_last_error. Shapes outside the
+ *              supported set return FA_ERR_UNSUPPORTED so the caller can
+ *              fall back to another implementation.
+ *   Threads    Calls are reentrant; calls that write the same buffers on
+ *              different streams race, as any two kernels would.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+  FA_FP32 = 0, /* IEEE binary32 */
+  FA_FP16 = 1, /* IEEE binary16 */
+  FA_BF16 = 2  /* bfloat16 */
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad dtype,
+                                  non-finite scale, misaligned pointer,
+                                  index overflow */
+  FA_ERR_UNSUPPORTED = 2,      /* valid request outside the supported set */
+  FA_ERR_WORKSPACE = 3,        /* backward workspace missing or too small */
+  FA_ERR_HIP = 4               /* the HIP runtime rejected a launch */
+} fa_status;
+
+/*
+ * fa_forward - fused attention forward.
+ *
+ * Computes, for every batch b and head h,
+ *   O[b,h]   = softmax(scale * Q[b,h] K[b,h]^T [+ causal mask]) V[b,h]
+ *   LSE[b,h,i] = ln sum_j exp(scale * Q[b,h,i] . K[b,h,j])  over the keys j
+ *                row i may see (natural log)
+ * ("From Self-Attention to FlashAttention", sections 1-2; "FlashAttention in
+ * ops-transformer", "Core idea" and "Online softmax"). LSE is the row
+ * statistic the backward recomputes probabilities from.
+ *
+ *   q, k, v  in   [B, H, N, D] of `dtype`
+ *   o        out  [B, H, N, D] of `dtype`, rounded to nearest even
+ *   lse      out  [B, H, N] fp32 (required)
+ *   B, H, N  >= 1
+ *   D        head dim; supported: 64, 128
+ *   scale    finite multiplier of Q K^T
+ *   causal   0 = full attention, non-zero = causal (keys 0..i for row i)
+ *   dtype    fa_dtype: FA_FP32, FA_FP16 or FA_BF16. Scores, softmax
+ *            statistics and the output accumulator are fp32 for every
+ *            dtype; for FA_FP16/FA_BF16 the probabilities are rounded to
+ *            the dtype only as the operand of the P V product.
+ *   stream   hipStream_t or NULL
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                     int dtype, void* stream);
+
+/*
+ * fa_backward_workspace_bytes - device workspace fa_backward needs for
+ * this shape: an fp32 dQ accumulator [B, H, N, D] and the fp32 row
+ * statistic delta [B, H, N], each padded to 256 bytes (the two-phase
+ * workspace query of "FlashAttention in ops-transformer", "Complete
+ * operator"). Returns 0 for non-positive sizes or on overflow.
+ */
+size_t fa_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+
+/*
+ * fa_backward - attention backward by recomputation.
+ *
+ * Given the forward's O and LSE and the upstream gradient dO, writes the
+ * exact gradients of the forward definition:
+ *   P  = exp(scale * Q K^T - LSE)        recomputed tile by tile, masked
+ *   dV = P^T dO
+ *   dP = dO V^T,  delta_i = sum_d dO[i,d] O[i,d]
+ *   dS = P * (dP - delta)
+ *   dQ = scale * dS K,   dK = scale * dS^T Q
+ * P is never stored ("Flash Attention algorithm design and I/O
+ * optimisation", "Core mechanism": save a few statistics, recompute local
+ * blocks; "FlashAttention in ops-transformer", "A surprise").
+ *
+ *   q, k, v, o, dout  in   [B, H, N, D] of `dtype`; o from fa_forward
+ *   lse               in   [B, H, N] fp32 from fa_forward
+ *   dq, dk, dv        out  [B, H, N, D] of `dtype`
+ *   workspace         device scratch of at least
+ *                     fa_backward_workspace_bytes(B, H, N, D) bytes, owned by
+ *                     the caller, 256-byte aligned; its contents on entry are
+ *                     ignored and on return unspecified
+ *   B, H, N, D, scale, causal, stream  as for fa_forward (same values)
+ *   dtype             FA_FP16 or FA_BF16 (FA_FP32 returns FA_ERR_UNSUPPORTED)
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED,
+ * FA_ERR_WORKSPACE or FA_ERR_HIP.
+ */
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                      int64_t N, int64_t D, float scale, int causal, int dtype,
+                      void* stream);
+
+/* fa_status_string - static, never-NULL name of a status code. */
+const char* fa_status_string(int status);
+
+/* fa_last_error - detail of the last failing call on the calling thread
+ * ("" if none). Valid until the next call on that thread. */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,81 @@
+"""Helpers shared by the GPU parity tests: error metrics, tolerances and
+oracle comparisons on selected (batch, head) pairs."""
+
+import math
+
+import numpy as np
+import torch
+
+import oracle.attention as orc
+
+# Tolerances on O (and dQ, dK, dV): fp32 max-abs 1e-5; half precision
+# max-abs 2e-2 and relative RMS 5e-3. LSE (fp32 for every dtype) is held to
+# 1e-4 absolute: its error comes from fp32 score accumulation and fp32
+# exp2/log2/sum over at most 2^14 keys (relative ~1e-6 .. 1e-5 on values of
+# order 10), independent of the dtype.
+TOL = {
+    "fp32": dict(max_abs=1e-5, rel_rms=None),
+    "bf16": dict(max_abs=2e-2, rel_rms=5e-3),
+    "fp16": dict(max_abs=2e-2, rel_rms=5e-3),
+}
+LSE_TOL = 1e-4
+
+TORCH_DTYPE = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to64(t):
+    return t.detach().to(torch.float32).cpu().to(torch.float64).numpy()
+
+
+def errors(x, ref):
+    d = x - ref
+    max_abs = float(np.abs(d).max()) if d.size else 0.0
+    den = math.sqrt(float(np.mean(ref * ref))) if d.size else 1.0
+    rel_rms = math.sqrt(float(np.mean(d * d))) / den if den > 0 else float(np.abs(d).max())
+    return max_abs, rel_rms
+
+
+def rep_floor(ref, dtype):
+    """max |cast(ref) - ref|: what rounding the exact result to dtype costs."""
+    t = torch.from_numpy(ref).to(TORCH_DTYPE[dtype]).to(torch.float64).numpy()
+    return float(np.abs(t - ref).max()) if ref.size else 0.0
+
+
+def assert_close(name, x, ref, dtype):
+    tol = TOL[dtype]
+    max_abs, rel_rms = errors(x, ref)
+    floor = rep_floor(ref, dtype)
+    msg = (f"{name}: max_abs={max_abs:.3e} (tol {tol['max_abs']:.0e}) rel_rms={rel_rms:.3e} "
+           f"(tol {tol['rel_rms']}) floor={floor:.3e}")
+    print(msg, flush=True)
+    assert np.all(np.isfinite(x)), name + ": non-finite values"
+    assert max_abs <= tol["max_abs"], msg
+    if tol["rel_rms"] is not None:
+        assert rel_rms <= tol["rel_rms"], msg
+    return max_abs, rel_rms
+
+
+def assert_lse_close(name, x, ref):
+    err = float(np.abs(x - ref).max()) if x.size else 0.0
+    print(f"{name}: lse max_abs={err:.3e} (tol {LSE_TOL:.0e})", flush=True)
+    assert np.all(np.isfinite(x)), name + ": non-finite LSE"
+    assert err <= LSE_TOL, f"{name}: lse max_abs {err:.3e} > {LSE_TOL}"
+
+
+def pick(t, heads):
+    """The selected (b, h) slices of a [B, H, ...] tensor as fp64 [1, n, ...]."""
+    return to64(torch.stack([t[b, h] for b, h in heads]))[None]
+
+
+def oracle_forward(q, k, v, scale, causal, heads):
+    q64, k64, v64 = (pick(t, heads) for t in (q, k, v))
+    return orc.attention_forward(q64, k64, v64, scale, causal)
+
+
+def oracle_backward(q, k, v, do, scale, causal, heads):
+    q64, k64, v64, g64 = (pick(t, heads) for t in (q, k, v, do))
+    return orc.attention_backward(q64, k64, v64, g64, scale, causal)
+
+
+def all_heads(B, H):
+    return [(b, h) for b in range(B) for h in range(H)]

@@ -1,0 +1,145 @@
+"""Forward parity on the GPU: the HIP kernels through the C ABI against the
+fp64 CPU oracle on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_113_amd as fa
+import workloads
+from gpu_util import (all_heads, assert_close, assert_lse_close, oracle_forward, pick, to64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run(q, k, v, causal, scale):
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(name, q, k, v, causal, scale, dtype, heads):
+    o, lse = run(q, k, v, causal, scale)
+    ro, rl = oracle_forward(q, k, v, scale, causal, heads)
+    assert_close(name + " O", pick(o, heads), ro, dtype)
+    assert_lse_close(name, pick(lse, heads), rl)
+    return o, lse
+
+
+def test_fp32_b1h2_n256_d64():
+    w = workloads.fp32_small()
+    q, k, v = workloads.make_inputs(w, device=DEV)
+    check(w.name, q, k, v, w.causal, w.scale, w.dtype, all_heads(w.B, w.H))
+
+
+def test_bf16_b2h8_n512_d64():
+    w = workloads.bf16_short()
+    q, k, v = workloads.make_inputs(w, device=DEV)
+    check(w.name, q, k, v, w.causal, w.scale, w.dtype, all_heads(w.B, w.H))
+
+
+def test_fp16_causal_b1h32_n4096_d128():
+    w = workloads.fp16_causal_4k()
+    q, k, v = workloads.make_inputs(w, device=DEV)
+    o, _ = check(w.name, q, k, v, w.causal, w.scale, w.dtype, [(0, 0), (0, 13), (0, 31)])
+    # Every head: causal row 0 attends to key 0 only, so O[0] = V[0] exactly.
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    assert torch.isfinite(o).all()
+
+
+@pytest.mark.parametrize("w", workloads.bf16_causal_sweep(), ids=lambda w: w.name)
+def test_bf16_causal_sweep(w):
+    q, k, v = workloads.make_inputs(w, device=DEV)
+    heads = [(0, 0), (0, 31)] if w.N <= 8192 else [(0, 17)]
+    o, _ = check(w.name, q, k, v, w.causal, w.scale, w.dtype, heads)
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    assert torch.isfinite(o).all()
+
+
+def test_bf16_training_forward_b4h16_n8192():
+    w = workloads.bf16_training()
+    q, k, v = workloads.make_inputs(w, with_grad_out=False, device=DEV)
+    o, _ = check(w.name + " fwd", q, k, v, w.causal, w.scale, w.dtype, [(0, 0), (3, 15)])
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+
+
+ODD_N = [1, 2, 7, 31, 33, 63, 65, 127, 129, 200, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(dtype, D, causal):
+    for N in ODD_N:
+        q, k, v = workloads.make_random((2, 3, N, D), seed=1000 + N, dtype=dtype, device=DEV)
+        check(f"{dtype} D{D} causal={causal} N{N}", q, k, v, causal, D ** -0.5, dtype,
+              all_heads(2, 3))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.02, 1.0])
+def test_scales(dtype, scale):
+    for causal in (False, True):
+        q, k, v = workloads.make_random((1, 2, 300, 64), seed=7, dtype=dtype, device=DEV)
+        o, lse = check(f"{dtype} scale={scale} causal={causal}", q, k, v, causal, scale, dtype,
+                       all_heads(1, 2))
+        if scale == 0.0:
+            # Uniform weights: LSE = ln(number of visible keys).
+            n = np.arange(1, 301) if causal else np.full(300, 300)
+            np.testing.assert_allclose(to64(lse)[0, 0], np.log(n), atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_large_inputs(dtype):
+    """Inputs x4 make raw scores of order 100: softmax in fp32 must not
+    overflow the 16-bit types."""
+    q, k, v = workloads.make_random((1, 2, 256, 128), seed=9, dtype=dtype, mult=4.0, device=DEV)
+    for causal in (False, True):
+        check(f"{dtype} x4 causal={causal}", q, k, v, causal, 128 ** -0.5, dtype, all_heads(1, 2))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_constant_v(dtype):
+    q, k, _ = workloads.make_random((1, 2, 333, 64), seed=11, dtype=dtype, device=DEV)
+    c = torch.linspace(-2, 2, 64).to(q.dtype).to(DEV)
+    v = c.expand(1, 2, 333, 64).contiguous()
+    for causal in (False, True):
+        o, _ = run(q, k, v, causal, 0.125)
+        tol = 1e-5 if dtype == "fp32" else 2e-2
+        assert float((o.float() - v.float()).abs().max()) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_deterministic(dtype):
+    q, k, v = workloads.make_random((2, 4, 1000, 128), seed=13, dtype=dtype, device=DEV)
+    for causal in (False, True):
+        o1, l1 = run(q, k, v, causal, 0.1)
+        o2, l2 = run(q, k, v, causal, 0.1)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_guard_bands(dtype):
+    """Outputs written in place inside larger buffers: nothing outside the
+    O and LSE regions changes."""
+    B, H, N, D = 2, 3, 77, 128
+    q, k, v = workloads.make_random((B, H, N, D), seed=15, dtype=dtype, device=DEV)
+    n_o, n_l, pad = B * H * N * D, B * H * N, 4096
+    obuf = torch.full((n_o + 2 * pad,), 7.0, dtype=q.dtype, device=DEV)
+    lbuf = torch.full((n_l + 2 * pad,), 7.0, dtype=torch.float32, device=DEV)
+    o = obuf[pad:pad + n_o].view(B, H, N, D)
+    lse = lbuf[pad:pad + n_l].view(B, H, N)
+    fa.forward(q, k, v, causal=True, scale=0.1, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((obuf[:pad] == 7).all()) and bool((obuf[pad + n_o:] == 7).all())
+    assert bool((lbuf[:pad] == 7).all()) and bool((lbuf[pad + n_l:] == 7).all())
+    ro, rl = oracle_forward(q, k, v, 0.1, True, all_heads(B, H))
+    assert_close("guarded O", pick(o, all_heads(B, H)), ro, dtype)
+
+
+def test_autograd_forward_matches():
+    q, k, v = workloads.make_random((1, 2, 64, 64), seed=17, dtype="bf16", device=DEV)
+    o = fa.attention(q, k, v, causal=True)
+    o2, _ = run(q, k, v, True, 0.125)
+    assert torch.equal(o, o2)
