@@ -26,12 +26,12 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- delta
 
-template <int D>
+template <typename TT, int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                            const uint16_t* __restrict__ dO,
                                                            float* __restrict__ delta,
                                                            float* __restrict__ dq_acc,
-                                                           int64_t rows, int is_bf16) {
+                                                           int64_t rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -42,22 +42,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
     const u32x4 g = *(const u32x4*)(dO + row * D + part * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float o0, o1, g0, g1;
-      if (is_bf16) {
-        o0 = __builtin_bit_cast(float, o[i] << 16);
-        o1 = __builtin_bit_cast(float, o[i] & 0xffff0000u);
-        g0 = __builtin_bit_cast(float, g[i] << 16);
-        g1 = __builtin_bit_cast(float, g[i] & 0xffff0000u);
-      } else {
-        const f16x2 oh = __builtin_bit_cast(f16x2, o[i]);
-        const f16x2 gh = __builtin_bit_cast(f16x2, g[i]);
-        o0 = (float)oh[0];
-        o1 = (float)oh[1];
-        g0 = (float)gh[0];
-        g1 = (float)gh[1];
-      }
-      acc = fmaf(o0, g0, acc);
-      acc = fmaf(o1, g1, acc);
+      acc = fmaf(TT::lo(o[i]), TT::lo(g[i]), acc);
+      acc = fmaf(TT::hi(o[i]), TT::hi(g[i]), acc);
     }
     float* z = dq_acc + row * D + part * 8;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -354,12 +340,11 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   float* dq_acc = (float*)(wsb + ws.dq_acc_off);
   float* delta = (float*)(wsb + ws.delta_off);
   const int64_t rows = a.B * a.H * a.N;
-  const int is_bf16 = a.dtype == FA_BF16;
 
   const int64_t pre_threads = rows * (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((pre_threads + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout,
-                     delta, dq_acc, rows, is_bf16);
+  hipLaunchKernelGGL((bwd_pre_kernel<TT, D>),
+                     dim3((unsigned)((pre_threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, delta, dq_acc, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -41,6 +41,10 @@ struct Bf16 {
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
   }
+  static __device__ __forceinline__ float lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return __builtin_bit_cast(float, x & 0xffff0000u);
+  }
 };
 
 // IEEE half inputs: same shape of MFMA, RNE packing.
@@ -54,6 +58,14 @@ struct F16 {
     r[0] = (_Float16)lo;
     r[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, r);
+  }
+  // Scalar half extraction (a bit_cast of a vector element to a 2 x half
+  // vector was folded to the first element by the compiler).
+  static __device__ __forceinline__ float lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
   }
 };
 

@@ -1,0 +1,173 @@
+// Fused attention forward for fp32 inputs on gfx950.
+//
+// Same online-softmax algorithm as the half-precision kernel ("From
+// Self-Attention to FlashAttention", section 2), computed with
+// v_mfma_f32_32x32x2_f32 so that nothing, probabilities included, is
+// rounded below fp32. One workgroup owns 128 query rows (32 per wave);
+// scores are computed transposed (S^T = K Q^T) so each lane pair holds one
+// query, and O^T = V^T P^T takes the probabilities straight from registers.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128;
+constexpr float kTau = 8.0f;
+
+// fp32 inputs: v_mfma_f32_32x32x2_f32 throughout, so nothing is rounded
+// below fp32 (probabilities included). Same transposed formulation as the
+// half-precision kernel with 32-key tiles.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, float c, float qsgn) {
+  constexpr int BN = 32;
+  constexpr int KSTR = D + 1;  // odd stride: the 32 rows read by a k-step hit 32 banks
+  constexpr int VSTR = D;
+  constexpr int DB = D / 32;
+  constexpr int KK = D / 2;
+  __shared__ float Ks[BN * KSTR];
+  __shared__ float Vs[BN * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int lq = lane & 31, hi = lane >> 5;
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int bh = logical / n_qtiles;
+  const int qt = n_qtiles - 1 - (logical % n_qtiles);
+  const int q0 = qt * kBM;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const float* Qh = Q + head;
+  const float* Kh = K + head;
+  const float* Vh = V + head;
+
+  const int qw0 = q0 + 32 * w;
+  const int qi = qw0 + lq;
+  float qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = (qi < N) ? qsgn * Qh[(size_t)qi * D + 2 * kk + hi] : 0.f;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mref = -INFINITY, lsum = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    for (int c4 = tid; c4 < BN * D / 4; c4 += kThreads) {
+      const int row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+      if (k0 + row < N) {
+        kx = *(const f32x4*)(Kh + (size_t)(k0 + row) * D + col);
+        vx = *(const f32x4*)(Vh + (size_t)(k0 + row) * D + col);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ks[row * KSTR + col + e] = kx[e];
+      *(f32x4*)(Vs + row * VSTR + col) = vx;
+    }
+    __syncthreads();
+
+    const bool active = k0 < N && (!CAUSAL || k0 <= qw0 + 31);
+    if (!active) continue;  // wave-uniform; barriers above are shared by all waves
+    const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw0);
+
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[lq * KSTR + 2 * kk + hi], qf[kk], s, 0, 0, 0);
+
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool ok = key < N && (!CAUSAL || key <= qi);
+        s[r] = ok ? s[r] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = half_swap_max(mx);
+    const float tmx = (mx == -INFINITY) ? -INFINITY : mx * c;
+    if (wave_any(tmx > mref + kTau)) {
+      const float mnew = fmaxf(mref, tmx);
+      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mref - mnew);
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = fast_exp2(fmaf(s[r], c, -mref));
+      if (need_mask) x = (s[r] == -INFINITY) ? 0.f : x;
+      p[r] = x;
+      lsum += x;
+    }
+    // O^T += V^T P^T, one key pair per MFMA: lane half hi carries key
+    // 8*(r/4) + 4*hi + (r%4) of register r in both operands.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VSTR + 32 * db + lq], p[r],
+                                                        oacc[db], 0, 0, 0);
+      }
+  }
+
+  const float ltot = half_swap_sum(lsum);
+  const float inv = 1.f / ltot;
+  if (qi < N) {
+    float* orow = O + head + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = oacc[db][4 * g4 + e] * inv;
+        *(f32x4*)(orow + 32 * db + 8 * g4 + 4 * hi) = out;
+      }
+    if (hi == 0) LSE[(size_t)bh * N + qi] = kLn2 * (mref + __log2f(ltot));
+  }
+}
+
+
+template <int D>
+hipError_t launch_f32(const FwdArgs& a, bool causal) {
+  const int n_qtiles = (int)((a.N + kBM - 1) / kBM);
+  const int64_t grid = (int64_t)n_qtiles * a.B * a.H;
+  const float c = fabsf(a.scale) * kLog2e;
+  const float qsgn = a.scale < 0.f ? -1.f : 1.f;
+  if (causal)
+    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o, a.lse, (int)a.N, n_qtiles, c, qsgn);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o, a.lse, (int)a.N, n_qtiles, c, qsgn);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_f32(const FwdArgs& a) {
+  const bool causal = a.causal != 0;
+  return a.D == 64 ? launch_f32<64>(a, causal) : launch_f32<128>(a, causal);
+}
+
+}  // namespace fa

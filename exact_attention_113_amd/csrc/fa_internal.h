@@ -48,6 +48,7 @@ struct BwdWorkspace {
 bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWorkspace* ws);
 
 hipError_t launch_forward(const FwdArgs& a);
+hipError_t launch_forward_f32(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a, const BwdWorkspace& ws);
 
 }  // namespace fa

@@ -41,15 +41,24 @@ def rep_floor(ref, dtype):
     return float(np.abs(t - ref).max()) if ref.size else 0.0
 
 
-def assert_close(name, x, ref, dtype):
+def assert_close(name, x, ref, dtype, strict=False):
+    """Element-wise comparison with the oracle.
+
+    strict=True applies the fixed bars (fp32 max-abs 1e-5; half precision
+    max-abs 2e-2 and rel-RMS 5e-3), as for the named workloads. Otherwise the
+    half-precision max-abs bar is widened by twice the representation floor
+    (max |cast(ref) - ref|), for edge cases whose outputs are large enough
+    that rounding them alone costs more than 2e-2.
+    """
     tol = TOL[dtype]
     max_abs, rel_rms = errors(x, ref)
     floor = rep_floor(ref, dtype)
-    msg = (f"{name}: max_abs={max_abs:.3e} (tol {tol['max_abs']:.0e}) rel_rms={rel_rms:.3e} "
+    tol_abs = tol["max_abs"] if (strict or dtype == "fp32") else tol["max_abs"] + 2 * floor
+    msg = (f"{name}: max_abs={max_abs:.3e} (tol {tol_abs:.2e}) rel_rms={rel_rms:.3e} "
            f"(tol {tol['rel_rms']}) floor={floor:.3e}")
     print(msg, flush=True)
     assert np.all(np.isfinite(x)), name + ": non-finite values"
-    assert max_abs <= tol["max_abs"], msg
+    assert max_abs <= tol_abs, msg
     if tol["rel_rms"] is not None:
         assert rel_rms <= tol["rel_rms"], msg
     return max_abs, rel_rms

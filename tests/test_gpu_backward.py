@@ -19,28 +19,33 @@ def run(q, k, v, do, causal, scale):
     return dq, dk, dv
 
 
-def check(name, q, k, v, do, causal, scale, dtype, heads):
+def check(name, q, k, v, do, causal, scale, dtype, heads, strict=False):
     dq, dk, dv = run(q, k, v, do, causal, scale)
     ref = oracle_backward(q, k, v, do, scale, causal, heads)
     for tag, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
-        assert_close(f"{name} {tag}", pick(got, heads), r, dtype)
+        assert_close(f"{name} {tag}", pick(got, heads), r, dtype, strict=strict)
     return dq, dk, dv
 
 
 def test_bf16_training_b4h16_n8192():
     w = workloads.bf16_training()
     q, k, v, do = workloads.make_inputs(w, device=DEV)
-    dq, dk, dv = check(w.name, q, k, v, do, w.causal, w.scale, w.dtype, [(0, 0), (3, 15)])
-    # Every head: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0, up to the
-    # rounding of P, dS and the outputs to bf16 (relative 2^-9 each).
-    u = 2.0 ** -9
+    dq, dk, dv = check(w.name, q, k, v, do, w.causal, w.scale, w.dtype, [(0, 0), (3, 15)],
+                       strict=True)
+    # Every head, every column: sum_j dV_j = sum_i dO_i (rows of P sum to 1)
+    # and sum_j dK_j = 0 (rows of dS sum to 0). Rounding P and dS to bf16 for
+    # the products, delta taken from the bf16 O, and bf16 outputs leave a
+    # residue far below the columns' norms; a masking or indexing error
+    # leaves one of the order of the norm.
     sdv = dv.double().sum(dim=2)
     sdo = do.double().sum(dim=2)
-    tol_v = 8 * u * (dv.double().pow(2).sum(dim=2).sqrt() + do.double().pow(2).sum(dim=2).sqrt())
-    assert bool(((sdv - sdo).abs() <= tol_v + 1e-3).all())
+    nv = dv.double().pow(2).sum(dim=2).sqrt()
+    rv = float(((sdv - sdo).abs() / nv).max())
     sdk = dk.double().sum(dim=2)
-    tol_k = 8 * u * dk.double().pow(2).sum(dim=2).sqrt()
-    assert bool((sdk.abs() <= tol_k + 1e-3).all())
+    nk = dk.double().pow(2).sum(dim=2).sqrt()
+    rk = float((sdk.abs() / nk).max())
+    print(f"max |sum dV - sum dO| / |dV| = {rv:.3e}; max |sum dK| / |dK| = {rk:.3e}", flush=True)
+    assert rv <= 0.05 and rk <= 0.05
 
 
 ODD_N = [1, 7, 33, 64, 65, 127, 129, 300]
