@@ -1,36 +1,42 @@
 // Fused attention forward for bf16/fp16 inputs on gfx950.
 //
 // One workgroup owns BM = 256 query rows of one (batch, head) and streams
-// the key/value rows through LDS in tiles of BN = 64 keys, keeping per
-// query row a running maximum, a running sum of exponentials and an
-// unnormalised fp32 output accumulator (online softmax: "From
-// Self-Attention to FlashAttention", section 2; "FlashAttention in
-// ops-transformer", "Core idea" and "Online softmax"). Scores and
-// probabilities live only in registers; O and the row logsumexp are the
-// only results written back ("only O is written to HBM", flowchart of
-// section 1 of the first page).
+// the key/value rows through LDS, keeping per query row a running maximum,
+// a running sum of exponentials and an unnormalised fp32 output accumulator
+// (online softmax: "From Self-Attention to FlashAttention", section 2;
+// "FlashAttention in ops-transformer", "Core idea" and "Online softmax").
+// Scores and probabilities live only in registers; O and the row
+// logsumexp are the only results written back (the flash data flow of
+// section 1 of the first page: only O goes back to HBM).
 //
-// Waves. Four waves of 64 query rows each: wave w owns the 32-row blocks
-// w and w + 4 of the workgroup's rows, so the four waves reach the causal
-// diagonal within a tile of each other. Scores are computed transposed,
-// S^T = K Q^T (32x32x16 MFMA, fp32 accumulate): lane j and j + 32 share one
-// query and each holds 16 of a 32-key block's scores, so row maxima and
-// sums are in-register reductions plus one exchange of the wave halves.
-// The output is accumulated transposed as well, O^T = V^T P^T, whose B
-// operand is the probability tile as the score MFMA left it in registers.
+// Waves. Eight waves, two per SIMD, each owning 32 consecutive query rows.
+// Scores are computed transposed, S^T = K Q^T (32x32x16 MFMA, fp32
+// accumulate): lane j and j + 32 share one query and each holds 16 of a
+// 32-key block's scores, so row maxima and sums are in-register reductions
+// plus one exchange of the wave halves. The output is accumulated
+// transposed as well, O^T = V^T P^T, whose B operand is the probability
+// tile as the score MFMA left it in registers.
 //
-// Memory path. K and V tiles (32 keys) go from global memory straight into LDS with
-// global_load_lds_dwordx4 (no staging registers), double-buffered: while a
-// tile is consumed the next one is in flight. Each 16-byte chunk of a row
-// is stored at an XOR-swizzled position so that the MFMA operand reads hit
-// distinct LDS banks. V stays row-major in LDS; its transposed A operand is
-// read with ds_read_b64_tr_b16, which hands lane i of each 16-lane group
+// Pipeline. Keys are processed in 32-key blocks. Step b issues the score
+// MFMAs of block b + 1 and the P V MFMAs of block b - 1 and, in between
+// them, the softmax of block b: the softmax depends on neither MFMA group,
+// so the matrix core and the vector ALU of a SIMD work at the same time,
+// within a wave and across the two waves sharing the SIMD. The accumulator
+// is rescaled lazily: a row's reference maximum moves only when a block's
+// maximum exceeds it by more than kTau (log2 units), so probabilities are
+// bounded by 2^kTau; the rescale (a rare, wave-uniform branch) is applied
+// before the next P V product.
+//
+// Memory path. K and V tiles of 64 keys go from global memory straight
+// into LDS with global_load_lds_dwordx4 (no staging registers), double
+// buffered, one barrier per tile. The four tile buffers are separate LDS
+// arrays addressed statically (the tile loop is unrolled by two), so the
+// compiler can tell that the operand reads of one buffer do not wait for
+// the direct loads still landing in another. Each 16-byte chunk of a row is
+// stored at an XOR-swizzled position so that the MFMA operand reads hit
+// distinct LDS banks. V stays row-major in LDS; its transposed A operand
+// is read with ds_read_b64_tr_b16, which hands lane i of each 16-lane group
 // element i%4 of the chunks addressed by lanes 4j + i/4 (j = 0..3).
-//
-// Pipeline. K runs one tile ahead of V: iteration t computes the scores of
-// tile t + 1 while it turns the scores of tile t into probabilities and
-// accumulates P V for tile t, so the score MFMAs and the softmax VALU work
-// are independent within an iteration. One barrier per tile.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -39,19 +45,18 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 512;  // 8 waves: two per SIMD
-constexpr int kWaves = kThreads / 64;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup: 32 per wave
-constexpr int kBN = 64;           // keys per tile: two 32-key MFMA blocks
-// Rescale the accumulator only when a row maximum grows by more than this
-// many powers of two; until then probabilities are taken against the older,
-// smaller reference, so each is at most 2^kTau. The final O = acc / sum and
-// LSE = ref + log2(sum) do not depend on which reference was used.
+constexpr int kWaves = 8;               // two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;        // query rows per workgroup (32 per wave)
+constexpr int kBN = 64;                 // keys per LDS tile
+constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+using False = std::false_type;
+using True = std::true_type;
 
 // Work-item order: heavier causal query tiles first (longest job first
 // over the CUs); when the heads divide evenly over the 8 XCDs each XCD
@@ -83,7 +88,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   constexpr int DB = D / 32;                  // 32-row blocks of the head dim
   constexpr int KK = D / 16;                  // k-steps of the score MFMA
   static_assert(LPW >= 1, "tile too small for one direct load per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -114,23 +122,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float mref = -INFINITY;  // reference maximum, log2 units
+  float mref = -INFINITY;  // reference maximum of the row, log2 units
   float lsum = 0.f;        // this lane's share of the row sum
+  float alpha = 1.f;       // pending rescale factor of the accumulator
+  bool rescale = false;    // wave-uniform: some lane's alpha differs from 1
 
+  // Key range of the workgroup and of this wave (causal: up to its last row).
   const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-  // First tile where this wave needs masks or block skipping: the causal
-  // diagonal of its rows, or the tile holding key N-1.
-  int first_edge = (N - 1) / kBN;
-  if (CAUSAL) first_edge = min(first_edge, (qw0 + 1) / kBN);
+  const int nb = (kv_end + kKB - 1) / kKB;  // 32-key steps of the workgroup
+  const int ntile = (kv_end + kBN - 1) / kBN;
+  const int wave_end = CAUSAL ? min(N, qw0 + 32) : N;
+  // Last step this wave computes (-1: every row of the wave is past N).
+  const int last_b = qw0 < N ? (wave_end - 1) / kKB : -1;
+  // First step whose scores need a mask: the block holding this wave's
+  // first diagonal key, or the partial block at the end of the keys.
+  int first_edge = (N % kKB) ? (N - 1) / kKB : nb;
+  if (CAUSAL) first_edge = min(first_edge, qw0 / kKB);
+  // Steps [1, interior_end) need neither masks nor drains.
+  const int interior_end = min(last_b + 1, first_edge);
 
-  char* const kbuf0 = smem;
-  char* const vbuf0 = smem + 2 * TILEB;
-
-  // Direct global->LDS load of rows [t*BN, t*BN + BN) of X. Lane l of load
-  // i writes row R0 + l/CH at chunk position l%CH, fetching the chunk that
-  // the swizzle puts there; rows past N repeat row N-1 (masked later).
-  auto load_tile = [&](const uint16_t* Xh, int t, char* dst, bool is_v) {
+  // Direct global->LDS load of rows [t*BN, t*BN + BN) of X into dst.
+  // Lane l of load i writes row R0 + l/CH at chunk position l%CH, fetching
+  // the chunk that the swizzle puts there; rows past N repeat row N-1
+  // (their scores are masked).
+  auto load_tile = [&](const uint16_t* Xh, int t, char* dst, bool is_v)
+      __attribute__((always_inline)) {
     const int k0 = t * kBN;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -145,127 +161,189 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
 
   // Per-lane parts of the LDS operand addresses.
   const int kxor = lq % CH;
+  const int koff = lq * ROWB;
   const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1;
   const int vlane = (4 * hi + tj) * ROWB + 8 * (tm & 1);
   const int vx = (2 * dsub + (tm >> 1)) ^ (2 * tj);
 
-  // One tile: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
-  auto tile = [&](auto edge, int t) {
-    constexpr bool EDGE = decltype(edge)::value;
-    const char* kt = kbuf0 + (t & 1) * TILEB;
-    const char* vt = vbuf0 + (t & 1) * TILEB;
-    const int k0 = t * kBN;
-    bool act[2];
+  // Scores of the 32-key half `half` of the K tile in kt: S^T = K Q^T.
+  auto scores = [&](const char* kt, int half, f32x16& s) __attribute__((always_inline)) {
+    const char* row = kt + 32 * half * ROWB + koff;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kbase = k0 + 32 * kb;
-      act[kb] = !EDGE || (kbase < N && (!CAUSAL || kbase <= qw0 + 31));
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 a = *(const u32x4*)(row + 16 * ((2 * kk + hi) ^ kxor));
+      s = TT::mma(a, qf[kk], s);
     }
+  };
 
-    f32x16 s[2];
+  // O^T += V^T P^T for the 32-key half `half` of the V tile in vt. Slot e
+  // of lane half hi in k-step h of the B operand is key
+  // 16*h + 4*hi + (e<4 ? e : e+4) of that half.
+  auto pv = [&](const char* vt, int half, const u32x4 (&pf)[2]) __attribute__((always_inline)) {
+    const char* base0 = vt + 32 * half * ROWB + vlane;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!act[kb]) continue;
-        const u32x4 a =
-            *(const u32x4*)(kt + (32 * kb + lq) * ROWB + 16 * ((2 * kk + hi) ^ kxor));
-        s[kb] = TT::mma(a, qf[kk], s[kb]);
+      for (int db = 0; db < DB; ++db) {
+        const char* base = base0 + 16 * h * ROWB + 16 * ((4 * db) ^ vx);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 u2 = __builtin_bit_cast(u32x2, up);
+        const u32x4 a = {l2[0], l2[1], u2[0], u2[1]};
+        oacc[db] = TT::mma(a, pf[h], oacc[db]);
       }
+  };
 
+  // Softmax of block b: mask (edge steps), row max, lazy reference update,
+  // probabilities packed as the B operands of the P V product, row sum.
+  auto softmax = [&](auto edge, int b, f32x16& s, u32x4 (&pf)[2]) __attribute__((always_inline)) {
+    constexpr bool EDGE = decltype(edge)::value;
+    // Edge steps: a key past N or (causal) after the row is excluded. Its
+    // score becomes -inf for the maximum and its probability exactly 0
+    // (not exp2(-inf * c), which is NaN when the scale is 0).
+    uint32_t okm = 0xffffu;
     if (EDGE) {
+      okm = 0;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = act[kb] && key < N && (!CAUSAL || key <= qi);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = kKB * b + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool ok = key < N && (!CAUSAL || key <= qi);
+        okm |= ok ? (1u << r) : 0u;
+        s[r] = ok ? s[r] : -INFINITY;
+      }
     }
-    float mx = s[0][0];
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = half_swap_max(mx);
-    const float tmx = (mx == -INFINITY) ? -INFINITY : mx * c;
-    if (wave_any(tmx > mref + kTau)) {
-      const float mnew = fmaxf(mref, tmx);
-      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mref - mnew);
-      mref = mnew;
-      lsum *= alpha;
+    // Block maximum in log2 units; a fully masked block stays -inf.
+    const float tmx = (EDGE && mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool need = tmx > mref + kTau;
+    const float mnew = need ? tmx : mref;
+    const float a = need ? fast_exp2(mref - mnew) : 1.f;  // exp2(-inf) = 0 at the start
+    alpha = a;
+    mref = mnew;
+    const float nm = -mnew;
+    float p[16];
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = fast_exp2(fmaf(s[r], c, nm));
+      if (EDGE) x = ((okm >> r) & 1u) ? x : 0.f;
+      p[r] = x;
+      sum += x;
+    }
+    lsum = fmaf(lsum, a, sum);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pf[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+    rescale = wave_any(need);
+  };
+
+  // Apply the pending rescale to the accumulator (before the next P V).
+  auto apply_rescale = [&]() __attribute__((always_inline)) {
+    if (rescale) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-
-    // Probabilities and the packed B operands of O^T += V^T P^T: slot e of
-    // lane half hi in step (kb, h) is key 32*kb + 16*h + 4*hi + (e<4 ? e : e+4).
-    const float nm = -mref;
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(fmaf(s[kb][r], c, nm));
-        if (EDGE) x = (s[kb][r] == -INFINITY) ? 0.f : x;
-        p[r] = x;
-        lsum += x;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pf[kb][h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
-    }
-
-    // The A operand (32 dims x 16 keys) is two transposing LDS reads.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* base = vt + (32 * kb + 16 * h) * ROWB + vlane + 16 * ((4 * db) ^ vx);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
-          const s16x4 up =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-          const u32x2 u2 = __builtin_bit_cast(u32x2, up);
-          const u32x4 a = {l2[0], l2[1], u2[0], u2[1]};
-          oacc[db] = TT::mma(a, pf[kb][h], oacc[db]);
-        }
-    }
   };
 
-  // Pipeline: tile t+1 is in flight into the other buffers while tile t is
-  // consumed; one barrier per tile makes the landed tile visible and frees
-  // the consumed buffers.
-  load_tile(Kh, 0, kbuf0, false);
-  load_tile(Vh, 0, vbuf0, true);
-  wait_vmem();
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) {
-      load_tile(Kh, t + 1, kbuf0 + ((t + 1) & 1) * TILEB, false);
-      load_tile(Vh, t + 1, vbuf0 + ((t + 1) & 1) * TILEB, true);
+  // Two score buffers and two probability buffers, used alternately by
+  // odd and even steps so that every index below is a compile-time one.
+  f32x16 sA, sB;
+  u32x4 pA[2], pB[2];
+
+  // One pipeline step: scores of block b+1 (K tile kt), P V of block b-1
+  // (V tile vt), softmax of block b. `cur` holds S(b) on entry, `nxt`
+  // receives S(b+1); `pprev` holds P(b-1), `pcur` receives P(b). The scores
+  // of the block after a wave's last one are computed and never used (they
+  // read a stale but in-bounds LDS buffer), which keeps the step free of
+  // branches.
+  auto step = [&](auto edge, auto has_pv, int b, const char* kt, const char* vt, f32x16& cur,
+                  f32x16& nxt, const u32x4 (&pprev)[2], u32x4 (&pcur)[2])
+      __attribute__((always_inline)) {
+    apply_rescale();
+    scores(kt, (b + 1) & 1, nxt);
+    if constexpr (decltype(has_pv)::value) pv(vt, (b - 1) & 1, pprev);
+    softmax(edge, b, cur, pcur);
+  };
+  // A step of a wave whose rows may need masks or be done: the full step
+  // while b is one of its steps, the last block's P V right after its last
+  // step, nothing afterwards (it still takes part in the barriers).
+  auto any_step = [&](int b, const char* kt, const char* vt, f32x16& cur, f32x16& nxt,
+                      const u32x4 (&pprev)[2], u32x4 (&pcur)[2]) __attribute__((always_inline)) {
+    if (b <= last_b) {
+      if (b >= first_edge) step(True{}, True{}, b, kt, vt, cur, nxt, pprev, pcur);
+      else step(False{}, True{}, b, kt, vt, cur, nxt, pprev, pcur);
+    } else if (b == last_b + 1) {
+      apply_rescale();
+      pv(vt, (b - 1) & 1, pprev);
     }
-    if (t < first_edge)
-      tile(std::false_type{}, t);
-    else
-      tile(std::true_type{}, t);
+  };
+  // Steps 2T+1 and 2T+2 read K tile T+1 (kt) and V tile T (vt): S(2T+1)
+  // is in sB and P(2T) in pA on entry.
+  auto tile_steps = [&](int T, const char* kt, const char* vt) __attribute__((always_inline)) {
+    const int b = 2 * T + 1;
+    if (b + 1 < interior_end) {
+      step(False{}, True{}, b, kt, vt, sB, sA, pA, pB);
+      step(False{}, True{}, b + 1, kt, vt, sA, sB, pB, pA);
+    } else {
+      any_step(b, kt, vt, sB, sA, pA, pB);
+      if (b + 1 < nb) any_step(b + 1, kt, vt, sA, sB, pB, pA);
+    }
+  };
+  // Barrier before step 2T+1: K tile T and V tile T-1 are no longer read
+  // and the loads issued at the previous barrier have landed; then K tile
+  // T+2 and V tile T+1 go out (into the buffers just freed).
+  auto tile_barrier = [&](int T, char* kdst, char* vdst) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
+    if (T + 2 < ntile) load_tile(Kh, T + 2, kdst, false);
+    if (T + 1 < ntile) load_tile(Vh, T + 1, vdst, true);
+  };
+
+  // Prologue: K tiles 0 and 1 and V tile 0, then the scores of block 0 and
+  // step 0 (no P V yet).
+  load_tile(Kh, 0, kb0, false);
+  load_tile(Vh, 0, vb0, true);
+  if (ntile > 1) load_tile(Kh, 1, kb1, false);
+  wait_vmem();
+  __syncthreads();
+  if (last_b >= 0) {
+    scores(kb0, 0, sA);
+    if (first_edge == 0) step(True{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
+    else step(False{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
   }
 
-  // Epilogue: O = acc / sum rounded to the dtype; LSE = ln 2 * (ref + log2 sum).
+  // Two tiles per iteration so that every buffer is named statically:
+  // even tiles T read K from kb1 and V from vb0, odd tiles K from kb0 and
+  // V from vb1.
+  for (int T = 0; 2 * T + 1 < nb; T += 2) {
+    tile_barrier(T, kb0, vb1);
+    tile_steps(T, kb1, vb0);
+    if (2 * T + 3 < nb) {
+      tile_barrier(T + 1, kb1, vb0);
+      tile_steps(T + 1, kb0, vb1);
+    }
+  }
+  // The last step's P V when it was the workgroup's last step (its V tile
+  // becomes visible at this barrier).
+  wait_vmem();
+  __syncthreads();
+  if (last_b == nb - 1 && last_b >= 0) {
+    apply_rescale();
+    const u32x4(&pl)[2] = (last_b & 1) ? pB : pA;
+    if ((last_b >> 1) & 1) pv(vb1, last_b & 1, pl);
+    else pv(vb0, last_b & 1, pl);
+  }
+
+  // O = acc / sum rounded to the dtype; LSE = ln 2 * (ref + log2 sum).
   const float ltot = half_swap_sum(lsum);
   const float inv = 1.f / ltot;
   if (qi < N) {
