@@ -51,12 +51,16 @@ constexpr int kBM = 32 * kWaves;        // query rows per workgroup (32 per wave
 constexpr int kBN = 64;                 // keys per LDS tile
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
+constexpr float kSumCap = 256.0f;       // 2^kTau
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 using False = std::false_type;
 using True = std::true_type;
+// Softmax kind of a step: False = interior block, True = block with masked
+// keys, Unmasked = full softmax without masks (a row's first block).
+struct Unmasked : std::false_type {};
 
 // Work-item order: heavier causal query tiles first (longest job first
 // over the CUs); when the heads divide evenly over the 8 XCDs each XCD
@@ -141,6 +145,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   // Steps [1, interior_end) need neither masks nor drains.
   const int interior_end = min(last_b + 1, first_edge);
 
+  // V chunk swizzle: the transposing reads of one half-wave cover four
+  // consecutive rows (r & 3 = 0..3) and four 16-byte chunks of each; the
+  // XOR spreads those rows over all 64 banks (256-byte rows, D = 128) or
+  // over both bank halves they alternate between (128-byte rows, D = 64).
+  auto vswz = [](int r) __attribute__((always_inline)) {
+    return CH == 16 ? 4 * (r & 3) : 2 * (r & 3);
+  };
+
   // Direct global->LDS load of rows [t*BN, t*BN + BN) of X into dst.
   // Lane l of load i writes row R0 + l/CH at chunk position l%CH, fetching
   // the chunk that the swizzle puts there; rows past N repeat row N-1
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     for (int i = 0; i < LPW; ++i) {
       const int R0 = (w * LPW + i) * RPI;
       const int r = R0 + lane / CH, p = lane % CH;
-      const int cg = is_v ? (p ^ (2 * (r & 3))) : (p ^ (r % CH));
+      const int cg = is_v ? (p ^ vswz(r)) : (p ^ (r % CH));
       const int grow = min(k0 + r, N - 1);
       __builtin_amdgcn_global_load_lds(Xh + (size_t)grow * D + cg * 8,
                                        (lds_void*)(dst + R0 * ROWB), 16, 0, 0);
@@ -164,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   const int koff = lq * ROWB;
   const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1;
   const int vlane = (4 * hi + tj) * ROWB + 8 * (tm & 1);
-  const int vx = (2 * dsub + (tm >> 1)) ^ (2 * tj);
+  const int vx = (2 * dsub + (tm >> 1)) ^ vswz(tj);
 
   // Scores of the 32-key half `half` of the K tile in kt: S^T = K Q^T.
   auto scores = [&](const char* kt, int half, f32x16& s) __attribute__((always_inline)) {
@@ -199,7 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
 
   // Softmax of block b: mask (edge steps), row max, lazy reference update,
   // probabilities packed as the B operands of the P V product, row sum.
-  auto softmax = [&](auto edge, int b, f32x16& s, u32x4 (&pf)[2]) __attribute__((always_inline)) {
+  auto softmax_full = [&](auto edge, int b, f32x16& s, u32x4 (&pf)[2])
+      __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge)::value;
     // Edge steps: a key past N or (causal) after the row is excluded. Its
     // score becomes -inf for the maximum and its probability exactly 0
@@ -242,6 +255,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) pf[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
     rescale = wave_any(need);
+  };
+
+  // Softmax of an interior block once the row's reference is set: the
+  // probabilities are taken against the current reference without a block
+  // maximum. A lane whose 16 probabilities sum to at most 2^kTau has none
+  // above 2^kTau, which is all the lazy rescaling needs; only when some lane
+  // of the wave exceeds that (a new, much larger maximum, or overflow to
+  // inf) is the block redone by the full softmax above, which moves the
+  // reference. The fast path ends with its results pinned so that they are
+  // computed here, interleaved with this step's MFMAs, and not moved past
+  // the rare branch.
+  auto softmax = [&](auto edge, int b, f32x16& s, u32x4 (&pf)[2]) __attribute__((always_inline)) {
+    using E = decltype(edge);
+    if constexpr (std::is_same<E, Unmasked>::value) {
+      softmax_full(False{}, b, s, pf);
+    } else if constexpr (E::value) {
+      softmax_full(True{}, b, s, pf);
+    } else {
+      const float nm = -mref;
+      float p[16];
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(s[r], c, nm));
+        sum += p[r];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pf[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+      const float lprev = lsum;
+      lsum = lprev + sum;
+      rescale = false;
+      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(lsum));
+      if (wave_any(!(sum <= kSumCap))) {
+        lsum = lprev;
+        softmax_full(False{}, b, s, pf);
+      }
+    }
   };
 
   // Apply the pending rescale to the accumulator (before the next P V).
@@ -317,8 +369,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   __syncthreads();
   if (last_b >= 0) {
     scores(kb0, 0, sA);
+    // Edge variant even without masks: the reference is not set yet, so
+    // step 0 takes the full softmax (with masks only where needed).
     if (first_edge == 0) step(True{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
-    else step(False{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
+    else step(Unmasked{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
   }
 
   // Two tiles per iteration so that every buffer is named statically:
