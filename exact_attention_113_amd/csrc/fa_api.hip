@@ -71,18 +71,18 @@ namespace fa {
 
 bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWorkspace* ws) {
   if (B < 1 || H < 1 || N < 1 || D < 1) return false;
-  int64_t rows = 0, elems = 0, acc = 0, dl = 0;
+  int64_t rows = 0, dl = 0;
   if (__builtin_mul_overflow(B, H, &rows) || __builtin_mul_overflow(rows, N, &rows) ||
-      __builtin_mul_overflow(rows, D, &elems) || __builtin_mul_overflow(elems, (int64_t)4, &acc) ||
       __builtin_mul_overflow(rows, (int64_t)4, &dl))
     return false;
   const int64_t round = 255;
-  if (acc > INT64_MAX - 2 * round - dl) return false;
-  ws->dq_acc_off = 0;
-  ws->dq_acc_bytes = (size_t)acc;
-  ws->delta_off = (size_t)((acc + round) & ~round);
+  if (dl > (INT64_MAX - 2 * round) / 2) return false;
+  const int64_t padded = (dl + round) & ~round;
+  ws->delta_off = 0;
   ws->delta_bytes = (size_t)dl;
-  ws->total = ws->delta_off + (size_t)((dl + round) & ~round);
+  ws->lse2_off = (size_t)padded;
+  ws->lse2_bytes = (size_t)dl;
+  ws->total = (size_t)(2 * padded);
   return true;
 }
 

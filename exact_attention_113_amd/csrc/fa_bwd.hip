@@ -8,32 +8,112 @@
 //   delta_i = sum_d dO[i,d] O[i,d], dS = P*(dP - delta),
 //   dQ = scale dS K, dK = scale dS^T Q.
 //
-// Three launches on the caller's stream:
-//   1. bwd_pre_kernel   delta for every row; zero the fp32 dQ accumulator.
-//   2. bwd_main_kernel  one workgroup per 128-key tile of one (batch, head):
-//                       K and V stay in registers, dK and dV accumulate in
-//                       registers over the query blocks that can see the
-//                       tile, and each block's dQ contribution is added to
-//                       the fp32 accumulator with atomics.
-//   3. bwd_dq_kernel    dQ accumulator -> dtype.
+// Three launches on the caller's stream, none with atomics, so the result
+// is bitwise reproducible (the "deterministic" option of "FlashAttention in
+// ops-transformer", "Complete operator", holds always):
+//   1. bwd_pre_kernel   delta and LSE*log2(e) for every row.
+//   2. bwd_dkdv_kernel  one workgroup per 128-key tile of one (batch, head),
+//                       iterating over 64-row query tiles that can see it.
+//                       Waves are paired on a SIMD: the first of a pair
+//                       computes S = Q K^T and P for its 32 keys and
+//                       accumulates dV^T += dO^T P; the second computes
+//                       dP = dO V^T, takes P from the first through LDS,
+//                       forms dS and accumulates dK^T += Q^T dS. Each wave
+//                       keeps one 32 x D accumulator and one operand tile in
+//                       registers.
+//   3. bwd_dq_kernel    one workgroup per 256-row query tile, streaming the
+//                       K and V tiles like the forward: S^T = K Q^T and
+//                       dP^T = V dO^T, dS, then dQ^T += K^T dS^T.
+//
+// Operand layouts (32x32x16 MFMA, see fa_device.h): a tile read row-wise
+// gives lane i + 32g the 8 values [row i][16k + 8g ..] of k-step k; a tile
+// read with ds_read_b64_tr_b16 gives lane j + 32g the values of column j at
+// rows {16h + 4g + 0..3, 16h + 8 + 4g + 0..3} of step h, which is the row
+// order in which a C-layout register block packs into an MFMA operand.
+// Tiles that are read both ways store their 16-byte chunks at the position
+// logical ^ swz(row), which keeps both kinds of read free of LDS bank
+// conflicts.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves, two per SIMD
+constexpr int kWaves = kThreads / 64;
 
-// ---------------------------------------------------------------- delta
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Chunk swizzle of a tile with CH 16-byte chunks per row. Row-wise reads
+// touch 16 consecutive rows at one logical chunk (a bijection over them);
+// transposed reads of a half-wave touch four consecutive rows and four
+// consecutive chunks (distinct chunk groups, or bank halves, per row).
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Direct global->LDS load of 64 rows [row0, row0 + 64) of a [N, D] matrix
+// into dst (rows past N repeat row N-1), each row swizzled by swz. All
+// waves of the workgroup take part.
+template <int D>
+__device__ __forceinline__ void load_rows64(const uint16_t* Xh, int row0, int N, char* dst, int w,
+                                            int lane) {
+  constexpr int CH = D / 8, ROWB = 2 * D, RPI = 64 / CH, LPW = 64 / (kWaves * RPI);
+  static_assert(LPW >= 1, "tile too small");
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int R0 = (w * LPW + i) * RPI;
+    const int r = R0 + lane / CH, p = lane % CH;
+    const int grow = min(row0 + r, N - 1);
+    const int cg = p ^ swz<CH>(r);  // logical chunk stored at position p
+    __builtin_amdgcn_global_load_lds((const void*)(Xh + (size_t)grow * D + cg * 8),
+                                     (lds_void*)(dst + R0 * ROWB), 16, 0, 0);
+  }
+}
+
+// Row-wise operand: lane (i + 32 hi), k-step kk -> row r0 + i, dims 16 kk + 8 hi ..
+template <int D>
+__device__ __forceinline__ u32x4 rd_row(const char* tile, int r0, int lq, int hi, int kk) {
+  constexpr int CH = D / 8, ROWB = 2 * D;
+  const int r = r0 + lq;
+  return *(const u32x4*)(tile + r * ROWB + 16 * ((2 * kk + hi) ^ swz<CH>(r)));
+}
+
+// Transposed operand: lane (j + 32 hi) -> column 32 db + j at rows
+// {r0 + 4hi + 0..3, r0 + 8 + 4hi + 0..3} (r0 a multiple of 16).
+template <int D>
+__device__ __forceinline__ u32x4 rd_tr(const char* tile, int r0, int lane, int db) {
+  constexpr int CH = D / 8, ROWB = 2 * D;
+  const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1, hi = lane >> 5;
+  const int c = 4 * db + 2 * dsub + (tm >> 1);
+  const int rlo = r0 + 4 * hi + tj, rup = rlo + 8;
+  const char* plo = tile + rlo * ROWB + 16 * (c ^ swz<CH>(rlo)) + 8 * (tm & 1);
+  const char* pup = tile + rup * ROWB + 16 * (c ^ swz<CH>(rup)) + 8 * (tm & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)plo);
+  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pup);
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 u2 = __builtin_bit_cast(u32x2, up);
+  return u32x4{l2[0], l2[1], u2[0], u2[1]};
+}
+
+// ---------------------------------------------------------------- delta, LSE
 
 template <typename TT, int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __restrict__ O,
-                                                           const uint16_t* __restrict__ dO,
-                                                           float* __restrict__ delta,
-                                                           float* __restrict__ dq_acc,
-                                                           int64_t rows) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ LSE,
+                                                      float* __restrict__ delta,
+                                                      float* __restrict__ lse2, int64_t rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
   const int part = (int)(gid % TPR);
   float acc = 0.f;
@@ -45,333 +125,445 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
       acc = fmaf(TT::lo(o[i]), TT::lo(g[i]), acc);
       acc = fmaf(TT::hi(o[i]), TT::hi(g[i]), acc);
     }
-    float* z = dq_acc + row * D + part * 8;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)z = zero;
-    *(f32x4*)(z + 4) = zero;
   }
   // Reduce over the TPR consecutive lanes of the row (TPR divides 64).
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
-// ---------------------------------------------------------------- main
+// ---------------------------------------------------------------- dK, dV
 
 template <typename TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ delta, float* __restrict__ dq_acc,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles, float c,
-    float dk_scale, float dq_scale, uint32_t qsign) {
-  constexpr int BK = 128;         // keys per workgroup: 32 per wave
-  constexpr int BM = 64;          // query rows per iteration: two 32-row blocks
-  constexpr int RSTR = D + 8;     // row-major Q / dO stride (elements)
-  constexpr int TSTR = BM + 4;    // transposed Q^T / dO^T stride
-  constexpr int KTSTR = BK + 8;   // K^T stride
-  constexpr int SSTR = BK + 8;    // dS stride
+    const float* __restrict__ LSE2, const float* __restrict__ DELTA, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int N, int n_ktiles, float c, float dk_scale, uint32_t qsign) {
+  constexpr int BK = 128;                // keys per workgroup: 32 per wave pair
+  constexpr int BM = 64;                 // query rows per iteration
+  constexpr int ROWB = 2 * D;
+  constexpr int TILEB = BM * ROWB;
   constexpr int DB = D / 32;
   constexpr int KK = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BM * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qts[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOts[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Kts[D * KTSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[BM * SSTR];
-  __shared__ float lse2s[BM];
-  __shared__ float dels[BM];
+  __shared__ __attribute__((aligned(1024))) char qt0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char qt1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char gt0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char gt1[TILEB];
+  __shared__ __attribute__((aligned(16))) float st0[2 * BM];  // lse2 then delta
+  __shared__ __attribute__((aligned(16))) float st1[2 * BM];
+  // P of each pair: [pair][q-block][4 x u32x4 per lane][64 lanes], fp32.
+  __shared__ __attribute__((aligned(16))) f32x4 pex[4 * 2 * 4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 31, hi = lane >> 5;
+  const int pair = w & 3;
+  const bool role_a = w < 4;  // S, P, dV; the other wave of the pair: dP, dS, dK
+
+  // Key tiles with the most query tiles first; heads pinned to XCDs.
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
   const int bh = logical / n_ktiles;
-  const int kt = logical % n_ktiles;  // low key tiles see the most queries: first
+  const int kt = logical % n_ktiles;
   const int k0 = kt * BK;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
   const uint16_t* dOh = dO + head;
-  const float* lseh = LSE + (size_t)bh * N;
-  const float* delh = delta + (size_t)bh * N;
-  float* dqh = dq_acc + head;
+  const float* lse2h = LSE2 + (size_t)bh * N;
+  const float* delh = DELTA + (size_t)bh * N;
 
-  // This wave's 32 keys as B operands (K for S = Q K^T, V for dP = dO V^T):
-  // lane (key lq, half hi), k-step kk -> row[16*kk + 8*hi + 0..7].
-  const int kw0 = k0 + 32 * w;
-  const int kidx = kw0 + lq;
-  u32x4 kf[KK], vf[KK];
+  // This pair's 32 keys as the B operand of S = Q K^T (role A) or of
+  // dP = dO V^T (role B): lane (key lq, half hi), k-step kk -> row[16kk + 8hi ..].
+  const int kw0 = k0 + 32 * pair;
+  const int key = kw0 + lq;
+  u32x4 bf[KK];
+  {
+    const uint16_t* Xh = (role_a ? K : V) + head;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (kidx < N) {
-      a = *(const u32x4*)(Kh + (size_t)kidx * D + 16 * kk + 8 * hi);
-      b = *(const u32x4*)(Vh + (size_t)kidx * D + 16 * kk + 8 * hi);
-    }
-    kf[kk] = a;
-    vf[kk] = b;
-  }
-  // K^T of the whole tile in LDS for dQ = dS K (4 keys x 8 dims per item).
-  for (int it = tid; it < (BK / 4) * (D / 8); it += kThreads) {
-    const int col = (it % (D / 8)) * 8, g = it / (D / 8);
-    u32x4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * g + j;
+    for (int kk = 0; kk < KK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < N) x = *(const u32x4*)(Kh + (size_t)key * D + col);
-      r[j] = x;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wi = e >> 1;
-      u32x2 out;
-      if ((e & 1) == 0) {
-        out[0] = (r[0][wi] & 0xffffu) | (r[1][wi] << 16);
-        out[1] = (r[2][wi] & 0xffffu) | (r[3][wi] << 16);
-      } else {
-        out[0] = (r[0][wi] >> 16) | (r[1][wi] & 0xffff0000u);
-        out[1] = (r[2][wi] >> 16) | (r[3][wi] & 0xffff0000u);
-      }
-      *(u32x2*)(Kts + (col + e) * KTSTR + 4 * g) = out;
+      if (key < N) x = *(const u32x4*)(Xh + (size_t)key * D + 16 * kk + 8 * hi);
+      // K sign-flipped for negative scale: S = Q (-K)^T (exact).
+      bf[kk] = role_a ? (x ^ qsign) : x;
     }
   }
-
-  f32x16 dk_acc[DB], dv_acc[DB];
+  f32x16 acc[DB];  // dV^T (role A) or dK^T (role B): lane = key, register = dim
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk_acc[i][r] = 0.f;
-      dv_acc[i][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   const int nq = (N + BM - 1) / BM;
-  const int qb_begin = CAUSAL ? (k0 / BM) : 0;
-  for (int qbk = qb_begin; qbk < nq; ++qbk) {
-    const int i0 = qbk * BM;
-    __syncthreads();
-    // Stage Q (sign-flipped for negative scale) and dO, both row-major and
-    // transposed, plus the rows' LSE (log2 units) and delta.
-    for (int it = tid; it < (BM / 4) * (D / 8); it += kThreads) {
-      const int col = (it % (D / 8)) * 8, g = it / (D / 8);
-      u32x4 rq[4], rg[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = i0 + 4 * g + j;
-        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-        if (row < N) {
-          x = *(const u32x4*)(Qh + (size_t)row * D + col) ^ qsign;
-          y = *(const u32x4*)(dOh + (size_t)row * D + col);
-        }
-        rq[j] = x;
-        rg[j] = y;
-        *(u32x4*)(Qs + (4 * g + j) * RSTR + col) = x;
-        *(u32x4*)(dOs + (4 * g + j) * RSTR + col) = y;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1;
-        u32x2 oq, og;
-        if ((e & 1) == 0) {
-          oq[0] = (rq[0][wi] & 0xffffu) | (rq[1][wi] << 16);
-          oq[1] = (rq[2][wi] & 0xffffu) | (rq[3][wi] << 16);
-          og[0] = (rg[0][wi] & 0xffffu) | (rg[1][wi] << 16);
-          og[1] = (rg[2][wi] & 0xffffu) | (rg[3][wi] << 16);
-        } else {
-          oq[0] = (rq[0][wi] >> 16) | (rq[1][wi] & 0xffff0000u);
-          oq[1] = (rq[2][wi] >> 16) | (rq[3][wi] & 0xffff0000u);
-          og[0] = (rg[0][wi] >> 16) | (rg[1][wi] & 0xffff0000u);
-          og[1] = (rg[2][wi] >> 16) | (rg[3][wi] & 0xffff0000u);
-        }
-        *(u32x2*)(Qts + (col + e) * TSTR + 4 * g) = oq;
-        *(u32x2*)(dOts + (col + e) * TSTR + 4 * g) = og;
-      }
-    }
-    if (tid < BM) {
-      const int row = i0 + tid;
-      lse2s[tid] = row < N ? lseh[row] * kLog2e : 0.f;
-      dels[tid] = row < N ? delh[row] : 0.f;
-    }
-    __syncthreads();
+  const int i_begin = CAUSAL ? (k0 / BM) : 0;
 
+  // Query tile i: Q and dO rows go straight to LDS; threads 0..127 fetch
+  // the tile's lse2 (0..63) and delta (64..127) values into a register,
+  // stored to LDS by store_stats once this iteration's reads are done.
+  auto load_qtile = [&] __device__ (int i, char* qd, char* gd) __attribute__((always_inline)) {
+    load_rows64<D>(Qh, i * BM, N, qd, w, lane);
+    load_rows64<D>(dOh, i * BM, N, gd, w, lane);
+    float v = 0.f;
+    if (tid < 2 * BM) {
+      const int row = min(i * BM + (tid & (BM - 1)), N - 1);
+      v = tid < BM ? lse2h[row] : delh[row];
+    }
+    return v;
+  };
+  auto store_stats = [&] __device__ (float* sd, float v) __attribute__((always_inline)) {
+    if (tid < 2 * BM) sd[tid] = v;
+  };
+
+  // Role A, phase 1: S = Q K^T for one 32-row query block, P (masked),
+  // P to LDS for the pair, P packed as the B operand of dV^T += dO^T P.
+  auto phase_a1 = [&] __device__ (auto masked, int i, const char* qt, const float* st, int qb,
+                      u32x4 (&pp)[2]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(masked)::value;
+    f32x16 s;
 #pragma unroll
-    for (int qb = 0; qb < BM / 32; ++qb) {
-      const int qbase = i0 + 32 * qb;
-      const bool active = kw0 < N && qbase < N && (!CAUSAL || qbase + 31 >= kw0);
-      if (!active) {
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          dSs[(32 * qb + 8 * (r >> 2) + 4 * hi + (r & 3)) * SSTR + 32 * w + lq] = 0;
-        continue;
-      }
-      // S and dP for 32 queries x this wave's 32 keys: lane = key,
-      // register r = query 8*(r/4) + 4*hi + r%4 of the block.
-      f32x16 s, dp;
+    for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(qt, 32 * qb, lq, hi, kk), bf[kk], s);
+    float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 l4 = *(const f32x4*)(st + 32 * qb + 8 * m + 4 * hi);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 aq = *(const u32x4*)(Qs + (32 * qb + lq) * RSTR + 16 * kk + 8 * hi);
-        const u32x4 ag = *(const u32x4*)(dOs + (32 * qb + lq) * RSTR + 16 * kk + 8 * hi);
-        s = TT::mma(aq, kf[kk], s);
-        dp = TT::mma(ag, vf[kk], dp);
-      }
-      float p[16], ds[16];
-      const bool need_mask = (kw0 + 31 >= N) || (qbase + 31 >= N) || (CAUSAL && kw0 + 31 > qbase);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float x = fast_exp2(fmaf(s[r], c, -lse2s[ql]));
-        if (need_mask) {
-          const int qidx = i0 + ql;
-          const bool ok = kidx < N && qidx < N && (!CAUSAL || kidx <= qidx);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * m + e;
+        float x = fast_exp2(fmaf(s[r], c, -l4[e]));
+        if (MASK) {
+          const int q = i * BM + 32 * qb + 8 * m + 4 * hi + e;
+          const bool ok = q < N && key < N && (!CAUSAL || key <= q);
           x = ok ? x : 0.f;
         }
         p[r] = x;
-        ds[r] = x * (dp[r] - dels[ql]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries:
-      // slot e of lane half hi in step h is query 16*h + 4*hi + (e<4 ? e : e+4).
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 pf, sf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pf[e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
-          sf[e] = TT::pack2(ds[8 * h + 2 * e], ds[8 * h + 2 * e + 1]);
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int toff = (32 * db + lq) * TSTR + 32 * qb + 16 * h + 4 * hi;
-          const u32x2 g0 = *(const u32x2*)(dOts + toff);
-          const u32x2 g1 = *(const u32x2*)(dOts + toff + 8);
-          const u32x2 q0 = *(const u32x2*)(Qts + toff);
-          const u32x2 q1 = *(const u32x2*)(Qts + toff + 8);
-          const u32x4 ag = {g0[0], g0[1], g1[0], g1[1]};
-          const u32x4 aq = {q0[0], q0[1], q1[0], q1[1]};
-          dv_acc[db] = TT::mma(ag, pf, dv_acc[db]);
-          dk_acc[db] = TT::mma(aq, sf, dk_acc[db]);
-        }
-      }
-      // dS (rounded to the dtype) into LDS, row = query, column = key.
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const uint32_t pk = TT::pack2(ds[r], ds[r + 1]);
-        const int ql = 32 * qb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        dSs[ql * SSTR + 32 * w + lq] = (uint16_t)(pk & 0xffffu);
-        dSs[(ql + 1) * SSTR + 32 * w + lq] = (uint16_t)(pk >> 16);
       }
     }
-    __syncthreads();
+    f32x4* dst = pex + ((pair * 2 + qb) * 4) * 64 + lane;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dst[64 * m] = f32x4{p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pp[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+  };
 
-    // dQ[i0 .. i0+BM) += scale * dS K over the tile's 128 keys. Output
-    // blocks (32 queries x 32 dims) are spread over the 4 waves.
-    constexpr int NBLK = (BM / 32) * DB;
+  // Role B, phase 1: dP = dO V^T for one query block.
+  auto phase_b1 = [&] __device__ (const char* gt, int qb, f32x16& dp) __attribute__((always_inline)) {
 #pragma unroll
-    for (int blk = w; blk < NBLK; blk += 4) {
-      const int qb = blk / DB, db = blk % DB;
-      if (i0 + 32 * qb >= N) continue;
-      f32x16 acc;
+    for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(gt, 32 * qb, lq, hi, kk), bf[kk], dp);
+  };
+
+  // Role A, phase 2: dV^T += dO^T P.
+  auto phase_a2 = [&] __device__ (const char* gt, int qb, const u32x4 (&pp)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const u32x4 a = *(const u32x4*)(dSs + (32 * qb + lq) * SSTR + 16 * kk + 8 * hi);
-        const u32x4 b = *(const u32x4*)(Kts + (32 * db + lq) * KTSTR + 16 * kk + 8 * hi);
-        acc = TT::mma(a, b, acc);
-      }
-      // A = dS (rows = queries), B = K (columns = this block's dims): acc[r]
-      // is dQ[query 8*(r/4)+4*hi+r%4][dim lq] of the block.
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qidx = i0 + 32 * qb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (qidx < N) atomicAdd(dqh + (size_t)qidx * D + 32 * db + lq, acc[r] * dq_scale);
-      }
+      for (int db = 0; db < DB; ++db)
+        acc[db] = TT::mma(rd_tr<D>(gt, 32 * qb + 16 * h, lane, db), pp[h], acc[db]);
+  };
+
+  // Role B, phase 2: dS = P (dP - delta), dK^T += Q^T dS.
+  auto phase_b2 = [&] __device__ (const char* qt, const float* st, int qb, const f32x16& dp)
+      __attribute__((always_inline)) {
+    const f32x4* src = pex + ((pair * 2 + qb) * 4) * 64 + lane;
+    float ds[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 p4 = src[64 * m];
+      const f32x4 d4 = *(const f32x4*)(st + BM + 32 * qb + 8 * m + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[4 * m + e] = p4[e] * (dp[4 * m + e] - d4[e]);
     }
-  }
+    u32x4 sp[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[h][e] = TT::pack2(ds[8 * h + 2 * e], ds[8 * h + 2 * e + 1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = TT::mma(rd_tr<D>(qt, 32 * qb + 16 * h, lane, db), sp[h], acc[db]);
+  };
 
-  // dK = scale * acc, dV = acc, rounded to the dtype. Lane lq holds key
-  // kidx; register r holds dim 32*db + 8*(r/4) + 4*hi + r%4.
-  if (kidx < N) {
-    uint16_t* dkr = dK + head + (size_t)kidx * D;
-    uint16_t* dvr = dV + head + (size_t)kidx * D;
+  // One query tile of one role: phase 1, barrier (P visible), phase 2.
+  auto iteration = [&] __device__ (auto is_a, int i, const char* qt, const char* gt, const float* st)
+      __attribute__((always_inline)) {
+    if constexpr (decltype(is_a)::value) {
+      const bool masked = (CAUSAL && i * BM < k0 + BK) || (i * BM + BM > N) || (k0 + BK > N);
+      u32x4 pp[2][2];
+      if (masked) {
+        phase_a1(std::true_type{}, i, qt, st, 0, pp[0]);
+        phase_a1(std::true_type{}, i, qt, st, 1, pp[1]);
+      } else {
+        phase_a1(std::false_type{}, i, qt, st, 0, pp[0]);
+        phase_a1(std::false_type{}, i, qt, st, 1, pp[1]);
+      }
+      __syncthreads();
+      phase_a2(gt, 0, pp[0]);
+      phase_a2(gt, 1, pp[1]);
+    } else {
+      f32x16 dp[2];
+      phase_b1(gt, 0, dp[0]);
+      phase_b1(gt, 1, dp[1]);
+      __syncthreads();
+      phase_b2(qt, st, 0, dp[0]);
+      phase_b2(qt, st, 1, dp[1]);
+    }
+  };
+
+  // Double-buffered query tiles, two per loop iteration so that every LDS
+  // buffer is named statically. The barrier at the end of an iteration
+  // makes the next tile (loaded during this one) visible and frees this
+  // tile's buffers and the P exchange area. The two roles run separate
+  // copies of the loop with the same barriers.
+  auto run = [&] __device__ (auto is_a) __attribute__((always_inline)) {
+    if (i_begin < nq) {
+      store_stats(st0, load_qtile(i_begin, qt0, gt0));
+      wait_vmem();
+      __syncthreads();
+    }
+    for (int i = i_begin; i < nq; i += 2) {
+      float v1 = 0.f;
+      if (i + 1 < nq) v1 = load_qtile(i + 1, qt1, gt1);
+      iteration(is_a, i, qt0, gt0, st0);
+      store_stats(st1, v1);
+      wait_vmem();
+      __syncthreads();
+      if (i + 1 >= nq) break;
+      float v0 = 0.f;
+      if (i + 2 < nq) v0 = load_qtile(i + 2, qt0, gt0);
+      iteration(is_a, i + 1, qt1, gt1, st1);
+      store_stats(st0, v0);
+      wait_vmem();
+      __syncthreads();
+    }
+  };
+  if (role_a) run(std::true_type{});
+  else run(std::false_type{});
+
+  // dK = scale * acc (role B), dV = acc (role A), rounded to the dtype. Lane
+  // lq holds key kw0 + lq; register r holds dim 32 db + 8(r/4) + 4 hi + r%4.
+  if (key < N) {
+    uint16_t* out = (role_a ? dV : dK) + head + (size_t)key * D;
+    const float sc = role_a ? 1.f : dk_scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 ok, ov;
-        ok[0] = TT::pack2(dk_acc[db][4 * g4] * dk_scale, dk_acc[db][4 * g4 + 1] * dk_scale);
-        ok[1] = TT::pack2(dk_acc[db][4 * g4 + 2] * dk_scale, dk_acc[db][4 * g4 + 3] * dk_scale);
-        ov[0] = TT::pack2(dv_acc[db][4 * g4], dv_acc[db][4 * g4 + 1]);
-        ov[1] = TT::pack2(dv_acc[db][4 * g4 + 2], dv_acc[db][4 * g4 + 3]);
-        *(u32x2*)(dkr + 32 * db + 8 * g4 + 4 * hi) = ok;
-        *(u32x2*)(dvr + 32 * db + 8 * g4 + 4 * hi) = ov;
+        u32x2 o;
+        o[0] = TT::pack2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc);
+        o[1] = TT::pack2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc);
+        *(u32x2*)(out + 32 * db + 8 * g4 + 4 * hi) = o;
       }
   }
 }
 
-// ---------------------------------------------------------------- dQ cast
+// ---------------------------------------------------------------- dQ
 
-template <typename TT>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const float* __restrict__ acc,
-                                                          uint16_t* __restrict__ dq,
-                                                          int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *(const f32x4*)(acc + 8 * i);
-  const f32x4 b = *(const f32x4*)(acc + 8 * i + 4);
-  u32x4 out;
-  out[0] = TT::pack2(a[0], a[1]);
-  out[1] = TT::pack2(a[2], a[3]);
-  out[2] = TT::pack2(b[0], b[1]);
-  out[3] = TT::pack2(b[2], b[3]);
-  *(u32x4*)(dq + 8 * i) = out;
+template <typename TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE2, const float* __restrict__ DELTA, uint16_t* __restrict__ dQ,
+    int N, int n_qtiles, float c, float dq_scale, uint32_t qsign) {
+  constexpr int BM = 32 * kWaves;  // query rows per workgroup
+  constexpr int BN = 64;           // keys per LDS tile
+  constexpr int ROWB = 2 * D;
+  constexpr int TILEB = BN * ROWB;
+  constexpr int DB = D / 32;
+  constexpr int KK = D / 16;
+  __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int lq = lane & 31, hi = lane >> 5;
+  // Heaviest causal query tiles first; heads pinned to XCDs.
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int bh = logical / n_qtiles;
+  const int qt = n_qtiles - 1 - logical % n_qtiles;
+  const int q0 = qt * BM;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+
+  // This wave's 32 rows of Q (sign-flipped for negative scale) and dO as B
+  // operands of S^T = K Q^T and dP^T = V dO^T, and the rows' statistics.
+  const int qw0 = q0 + 32 * w;
+  const int qi = qw0 + lq;
+  u32x4 qf[KK], gf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (qi < N) {
+      x = *(const u32x4*)(Q + head + (size_t)qi * D + 16 * kk + 8 * hi);
+      y = *(const u32x4*)(dO + head + (size_t)qi * D + 16 * kk + 8 * hi);
+    }
+    qf[kk] = x ^ qsign;
+    gf[kk] = y;
+  }
+  const float l2 = qi < N ? LSE2[(size_t)bh * N + qi] : 0.f;
+  const float dl = qi < N ? DELTA[(size_t)bh * N + qi] : 0.f;
+
+  f32x16 acc[DB];  // dQ^T: lane = query, register = dim
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntile = (kv_end + BN - 1) / BN;
+  const int wave_end = CAUSAL ? min(N, qw0 + 32) : N;
+  const int last_b = qw0 < N ? (wave_end - 1) / 32 : -1;  // last 32-key block of this wave
+  int first_edge = (N % 32) ? (N - 1) / 32 : (kv_end + 31) / 32;
+  if (CAUSAL) first_edge = min(first_edge, qw0 / 32);
+
+  // One 32-key block (half of the tile in kt/vt).
+  auto block = [&] __device__ (auto masked, int b, const char* kt, const char* vt)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(masked)::value;
+    const int half = b & 1;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+    // The two products one after the other (fenced), so that at most one
+    // set of operand fragments is live at a time.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(kt, 32 * half, lq, hi, kk), qf[kk], s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(vt, 32 * half, lq, hi, kk), gf[kk], dp);
+    __builtin_amdgcn_sched_barrier(0);
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(s[r], c, -l2));
+      if (MASK) {
+        const int kidx = 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool ok = kidx < N && (!CAUSAL || kidx <= qi);
+        p = ok ? p : 0.f;
+      }
+      ds[r] = p * (dp[r] - dl);
+    }
+    u32x4 sp[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[h][e] = TT::pack2(ds[8 * h + 2 * e], ds[8 * h + 2 * e + 1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = TT::mma(rd_tr<D>(kt, 32 * half + 16 * h, lane, db), sp[h], acc[db]);
+  };
+  auto any_block = [&] __device__ (int b, const char* kt, const char* vt) __attribute__((always_inline)) {
+    if (b > last_b) return;
+    if (b >= first_edge) block(std::true_type{}, b, kt, vt);
+    else block(std::false_type{}, b, kt, vt);
+  };
+
+  load_rows64<D>(Kh, 0, N, kb0, w, lane);
+  load_rows64<D>(Vh, 0, N, vb0, w, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < ntile; t += 2) {
+    if (t + 1 < ntile) {
+      load_rows64<D>(Kh, (t + 1) * BN, N, kb1, w, lane);
+      load_rows64<D>(Vh, (t + 1) * BN, N, vb1, w, lane);
+    }
+    any_block(2 * t, kb0, vb0);
+    any_block(2 * t + 1, kb0, vb0);
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 >= ntile) break;
+    if (t + 2 < ntile) {
+      load_rows64<D>(Kh, (t + 2) * BN, N, kb0, w, lane);
+      load_rows64<D>(Vh, (t + 2) * BN, N, vb0, w, lane);
+    }
+    any_block(2 * t + 2, kb1, vb1);
+    any_block(2 * t + 3, kb1, vb1);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // dQ = scale * acc, rounded to the dtype: lane lq holds query qi; register
+  // r holds dim 32 db + 8(r/4) + 4 hi + r%4.
+  if (qi < N) {
+    uint16_t* out = dQ + head + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 o;
+        o[0] = TT::pack2(acc[db][4 * g4] * dq_scale, acc[db][4 * g4 + 1] * dq_scale);
+        o[1] = TT::pack2(acc[db][4 * g4 + 2] * dq_scale, acc[db][4 * g4 + 3] * dq_scale);
+        *(u32x2*)(out + 32 * db + 8 * g4 + 4 * hi) = o;
+      }
+  }
 }
 
 template <typename TT, int D>
 hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   char* wsb = (char*)a.workspace;
-  float* dq_acc = (float*)(wsb + ws.dq_acc_off);
   float* delta = (float*)(wsb + ws.delta_off);
+  float* lse2 = (float*)(wsb + ws.lse2_off);
   const int64_t rows = a.B * a.H * a.N;
 
   const int64_t pre_threads = rows * (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<TT, D>),
-                     dim3((unsigned)((pre_threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, delta, dq_acc, rows);
+  hipLaunchKernelGGL((bwd_pre_kernel<TT, D>), dim3((unsigned)((pre_threads + 255) / 256)),
+                     dim3(256), 0, a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
+                     delta, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int n_ktiles = (int)((a.N + 127) / 128);
-  const int64_t grid = (int64_t)n_ktiles * a.B * a.H;
   const float c = fabsf(a.scale) * kLog2e;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  // Q is staged sign-flipped when scale < 0, so dK = |scale| dS^T (-Q) ...
-  // = scale dS^T Q; dQ = scale dS K does not involve Q.
-  const float dk_scale = fabsf(a.scale);
+  // For scale < 0 the scores are formed from -K (dK/dV kernel) or -Q (dQ
+  // kernel) with |scale|; the gradients dK = scale dS^T Q and dQ = scale dS K
+  // use the unflipped operands.
+  const float dk_scale = a.scale;
   const float dq_scale = a.scale;
+  const int bh = (int)(a.B * a.H);
+
+  const int n_ktiles = (int)((a.N + 127) / 128);
+  const dim3 g1((unsigned)((int64_t)n_ktiles * bh));
   if (a.causal)
-    hipLaunchKernelGGL((bwd_main_kernel<TT, D, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, delta, dq_acc, (uint16_t*)a.dk,
-                       (uint16_t*)a.dv, (int)a.N, n_ktiles, c, dk_scale, dq_scale, qsign);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, true>), g1, dim3(kThreads), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       (int)a.N, n_ktiles, c, dk_scale, qsign);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<TT, D, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, delta, dq_acc, (uint16_t*)a.dk,
-                       (uint16_t*)a.dv, (int)a.N, n_ktiles, c, dk_scale, dq_scale, qsign);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, false>), g1, dim3(kThreads), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       (int)a.N, n_ktiles, c, dk_scale, qsign);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int64_t n8 = rows * D / 8;
-  hipLaunchKernelGGL((bwd_dq_kernel<TT>), dim3((unsigned)((n8 + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, a.stream, dq_acc, (uint16_t*)a.dq, n8);
+  const int n_qtiles = (int)((a.N + 255) / 256);
+  const dim3 g2((unsigned)((int64_t)n_qtiles * bh));
+  if (a.causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, true>), g2, dim3(kThreads), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dq, (int)a.N, n_qtiles,
+                       c, dq_scale, qsign);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, false>), g2, dim3(kThreads), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dq, (int)a.N, n_qtiles,
+                       c, dq_scale, qsign);
   return hipGetLastError();
 }
 

@@ -41,8 +41,8 @@ struct BwdArgs {
 
 // Byte offsets of the backward workspace's parts (each 256-byte aligned).
 struct BwdWorkspace {
-  size_t dq_acc_off, dq_acc_bytes;  // fp32 [B, H, N, D]
-  size_t delta_off, delta_bytes;    // fp32 [B, H, N]
+  size_t delta_off, delta_bytes;    // fp32 [B, H, N]: sum_d dO * O
+  size_t lse2_off, lse2_bytes;      // fp32 [B, H, N]: LSE * log2(e)
   size_t total;
 };
 bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWorkspace* ws);

@@ -101,10 +101,10 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * fa_backward_workspace_bytes - device workspace fa_backward needs for
- * this shape: an fp32 dQ accumulator [B, H, N, D] and the fp32 row
- * statistic delta [B, H, N], each padded to 256 bytes (the two-phase
- * workspace query of "FlashAttention in ops-transformer", "Complete
- * operator"). Returns 0 for non-positive sizes or on overflow.
+ * this shape: two fp32 row statistics [B, H, N] (delta = rowsum(dO * O) and
+ * LSE * log2(e)), each padded to 256 bytes (the two-phase workspace query of
+ * "FlashAttention in ops-transformer", "Complete operator"). Returns 0 for
+ * non-positive sizes or on overflow.
  */
 size_t fa_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
 
@@ -120,7 +120,10 @@ size_t fa_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  *   dQ = scale * dS K,   dK = scale * dS^T Q
  * P is never stored ("Flash Attention algorithm design and I/O
  * optimisation", "Core mechanism": save a few statistics, recompute local
- * blocks; "FlashAttention in ops-transformer", "A surprise").
+ * blocks; "FlashAttention in ops-transformer", "A surprise"). No step uses
+ * atomics: the gradients are bitwise reproducible from run to run (the
+ * deterministic mode of "FlashAttention in ops-transformer", "Complete
+ * operator", is the only mode).
  *
  *   q, k, v, o, dout  in   [B, H, N, D] of `dtype`; o from fa_forward
  *   lse               in   [B, H, N] fp32 from fa_forward

@@ -106,10 +106,10 @@ def test_backward_validation(kw, status):
 
 def test_workspace_bytes():
     lib = _lib.load()
-    # fp32 dQ accumulator [B,H,N,D] then fp32 delta [B,H,N], each padded to 256 B.
+    # fp32 delta [B,H,N] then fp32 LSE*log2(e) [B,H,N], each padded to 256 B.
     def expect(B, H, N, D):
         pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        return pad(4 * B * H * N * D) + pad(4 * B * H * N)
+        return 2 * pad(4 * B * H * N)
     for shape in [(1, 1, 1, 64), (4, 16, 8192, 128), (2, 3, 7, 128), (1, 1, 1000, 64)]:
         assert lib.fa_backward_workspace_bytes(*shape) == expect(*shape)
     assert lib.fa_backward_workspace_bytes(0, 1, 1, 64) == 0

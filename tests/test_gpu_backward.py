@@ -92,3 +92,41 @@ def test_autograd_matches_backward():
     for got, r in zip((qa.grad, ka.grad, va.grad), ref):
         assert_close("autograd", pick(got, all_heads(1, 2)), r, "bf16")
     assert np.isfinite(to64(dq)).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_deterministic(causal):
+    """No atomics anywhere: two backward passes give bitwise equal gradients
+    ("FlashAttention in ops-transformer", "Complete operator": the
+    deterministic option)."""
+    q, k, v, do = workloads.make_random((2, 4, 1000, 128), seed=27, dtype="bf16", count=4,
+                                        device=DEV)
+    g1 = run(q, k, v, do, causal, 0.1)
+    g2 = run(q, k, v, do, causal, 0.1)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_workspace_reuse_and_guard_bands():
+    """A dirty, oversized workspace is accepted and gradients written in place
+    inside larger buffers leave everything around them untouched."""
+    B, H, N, D = 1, 2, 130, 64
+    q, k, v, do = workloads.make_random((B, H, N, D), seed=29, dtype="bf16", count=4, device=DEV)
+    o, lse = fa.forward(q, k, v, causal=True, scale=0.125)
+    need = fa.backward_workspace_bytes(B, H, N, D)
+    ws = torch.full((need + 4096,), 0x7f, dtype=torch.uint8, device=DEV)
+    n, pad = B * H * N * D, 2048
+    bufs = [torch.full((n + 2 * pad,), 5.0, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    outs = [b[pad:pad + n].view(B, H, N, D) for b in bufs]
+    lib = fa._lib.load()
+    st = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                         outs[2].data_ptr(), ws.data_ptr(), ws.numel(), B, H, N, D, 0.125, 1,
+                         fa._lib.FA_BF16, None)
+    torch.cuda.synchronize()
+    assert st == 0
+    for b in bufs:
+        assert bool((b[:pad] == 5).all()) and bool((b[pad + n:] == 5).all())
+    ref = oracle_backward(q, k, v, do, 0.125, True, all_heads(B, H))
+    for tag, got, r in zip(("dQ", "dK", "dV"), outs, ref):
+        assert_close(f"in-place {tag}", pick(got, all_heads(B, H)), r, "bf16")
