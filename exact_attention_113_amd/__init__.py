@@ -8,6 +8,7 @@ kernels; there is no fallback path.
     o, lse = forward(q, k, v, causal=False, scale=None)
     dq, dk, dv = backward(q, k, v, o, lse, do, causal=False, scale=None)
     o = attention(q, k, v, causal=False, scale=None)   # autograd-aware
+    o, lse = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None)
 
 Tensors are contiguous [B, H, N, D] of float32, float16 or bfloat16 on the
 GPU; the default scale is 1/sqrt(D).
@@ -65,6 +66,43 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
                             lse.data_ptr(), B, H, N, D, float(scale), int(bool(causal)),
                             _DTYPES[q.dtype], _stream_handle(q))
     _lib.check("fa_forward", st)
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out=None,
+                   lse=None):
+    """Forward over a packed batch of variable-length sequences with grouped K/V heads.
+
+    q: [total, H, D]; k, v: [total, H_kv, D] (H_kv divides H); cu_seqlens: int32
+    [batch + 1] on q's device, sequence b being tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
+    Returns (o [total, H, D], lse fp32 [H, total]).
+    """
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[0] != k.shape[0] \
+            or q.shape[2] != k.shape[2]:
+        raise ValueError(f"need q [total, H, D] and k, v [total, H_kv, D], got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or \
+            v.dtype != q.dtype:
+        raise TypeError("dtype must be float16 or bfloat16 (all equal)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [batch + 1]")
+    total, H, D = q.shape
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                   int(max_seqlen), total, H, k.shape[1], D, float(scale),
+                                   int(bool(causal)), _DTYPES[q.dtype], _stream_handle(q))
+    _lib.check("fa_forward_varlen", st)
     return out, lse
 
 

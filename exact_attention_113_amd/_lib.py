@@ -13,6 +13,8 @@ FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP
 _P, _I64, _F, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
 PROTOTYPES = {
     "fa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _I, _I, _P]),
+    "fa_forward_varlen": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                         _I64, _F, _I, _I, _P]),
     "fa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "fa_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64,
                                    _I64, _I64, _F, _I, _I, _P]),

@@ -102,8 +102,46 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: lse must be 4-byte aligned");
   fa_status s = check_shape(B, H, N, D, scale, dtype);
   if (s != FA_OK) return s;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, D, scale, causal, dtype, (hipStream_t)stream};
+  fa::FwdArgs a{q,     k,      v,     o,     lse, B, H, N, D, scale, causal, dtype, (hipStream_t)stream,
+                H,     nullptr, 0};
   return hip_status(fa::launch_forward(a), "fa_forward");
+}
+
+fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int64_t batch, int64_t max_seqlen,
+                            int64_t total, int64_t H, int64_t H_kv, int64_t D, float scale,
+                            int causal, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !o || !lse || !cu_seqlens)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_forward_varlen: q, k, v, o, lse and cu_seqlens must be non-NULL");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward_varlen: q, k, v, o must be 16-byte aligned");
+  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_forward_varlen: lse and cu_seqlens must be 4-byte aligned");
+  if (batch < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward_varlen: batch must be >= 1 (got %lld)",
+                (long long)batch);
+  if (H_kv < 1 || H < 1 || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_forward_varlen: H (%lld) must be a positive multiple of H_kv (%lld)",
+                (long long)H, (long long)H_kv);
+  if (total < 1 || max_seqlen < 1 || max_seqlen > total)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_forward_varlen: need 1 <= max_seqlen (%lld) <= total (%lld)",
+                (long long)max_seqlen, (long long)total);
+  fa_status s = check_shape(1, H, total, D, scale, dtype);
+  if (s != FA_OK) return s;
+  if (dtype == FA_FP32)
+    return fail(FA_ERR_UNSUPPORTED, "fa_forward_varlen: fp32 is not supported");
+  const int64_t wgs = ((max_seqlen + 255) / 256) * batch * H;
+  if (batch > (int64_t)1 << 30 || wgs > (int64_t)0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "fa_forward_varlen: %lld workgroups exceed one grid",
+                (long long)wgs);
+  fa::FwdArgs a{q,     k,      v,     o,      lse,        batch, H,     max_seqlen, D,
+                scale, causal, dtype, (hipStream_t)stream, H_kv, cu_seqlens, total};
+  return hip_status(fa::launch_forward(a), "fa_forward_varlen");
 }
 
 size_t fa_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {

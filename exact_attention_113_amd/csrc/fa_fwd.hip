@@ -63,27 +63,50 @@ using True = std::true_type;
 struct Unmasked : std::false_type {};
 
 // Work-item order: heavier causal query tiles first (longest job first
-// over the CUs); when the heads divide evenly over the 8 XCDs each XCD
-// keeps the same BH/8 heads, so their K and V stay in that XCD's L2.
-__device__ __forceinline__ void tile_of(int lin, int n_qtiles, int bh_count, int& qt, int& bh) {
+// over the CUs). The (sequence, head) pairs are numbered head-major,
+// p = h * batch + b; when they divide evenly over the 8 XCDs, each XCD
+// keeps one contiguous range of p: the same heads of every sequence. Their
+// K and V stay in that XCD's L2 (with grouped heads, the query heads of one
+// K/V head land together), and sequences of unequal length spread over all
+// XCDs instead of loading some more than others.
+__device__ __forceinline__ void tile_of(int lin, int n_qtiles, int bh_count, int& qt, int& p) {
   if ((bh_count & 7) == 0) {
     const int hpx = bh_count >> 3;
     const int xcd = lin & 7, slot = lin >> 3;
     qt = n_qtiles - 1 - slot / hpx;
-    bh = xcd * hpx + slot % hpx;
+    p = xcd * hpx + slot % hpx;
   } else {
     qt = n_qtiles - 1 - lin / bh_count;
-    bh = lin % bh_count;
+    p = lin % bh_count;
   }
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Kernel arguments. Dense: Q, K, V, O are [B, H, N, D] and LSE [B, H, N].
+// Packed variable-length batches (cu != null): Q and O are [total, H, D], K
+// and V [total, H / group, D], LSE [H, total]; sequence b holds tokens
+// [cu[b], cu[b+1]). Query head h reads K/V head h / group in both layouts.
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* cu;  // sequence starts (batch + 1 entries) or null
+  int seqlen;         // dense: N; packed: the longest sequence
+  int total;          // packed: tokens in the batch
+  int heads;          // query heads
+  int group;          // query heads per K/V head
+  int n_qtiles;
+  int bh_count;
+  float c;
+  uint32_t qsign;
+};
+
 template <typename TT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
-    int n_qtiles, int bh_count, float c, uint32_t qsign) {
+    const FwdParams prm) {
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                 // bytes per row
   constexpr int TILEB = kBN * ROWB;           // bytes per K or V tile
@@ -101,13 +124,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 31, hi = lane >> 5;
 
-  int qt, bh;
-  tile_of(blockIdx.x, n_qtiles, bh_count, qt, bh);
+  const float c = prm.c;
+  const uint32_t qsign = prm.qsign;
+  int qt, p;
+  tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, qt, p);
   const int q0 = qt * kBM;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  // This (sequence, head): its length N, the element offsets of its first
+  // Q/O and K/V rows and of its LSE entries, and the row strides.
+  const int batch = prm.bh_count / prm.heads;
+  const int h = p / batch, bidx = p - h * batch;
+  const int bh = bidx * prm.heads + h;
+  const int hkv = prm.heads / prm.group, hk = h / prm.group;
+  int N;
+  size_t qbase, kvbase, lbase;
+  size_t sq, skv;
+  if (prm.cu) {
+    const int s0 = min(max(prm.cu[bidx], 0), prm.total);
+    const int s1 = min(max(prm.cu[bidx + 1], s0), prm.total);
+    N = min(s1 - s0, prm.seqlen);
+    qbase = ((size_t)s0 * prm.heads + h) * D;
+    kvbase = ((size_t)s0 * hkv + hk) * D;
+    lbase = (size_t)h * prm.total + s0;
+    sq = (size_t)prm.heads * D;
+    skv = (size_t)hkv * D;
+  } else {
+    N = prm.seqlen;
+    qbase = (size_t)bh * N * D;
+    kvbase = ((size_t)bidx * hkv + hk) * N * D;
+    lbase = (size_t)bh * N;
+    sq = skv = D;
+  }
+  if (q0 >= N) return;  // a tile past the end of a shorter sequence: no work
+  const uint16_t* Qh = prm.q + qbase;
+  const uint16_t* Kh = prm.k + kvbase;
+  const uint16_t* Vh = prm.v + kvbase;
 
   // This wave's 32 query rows and their B operands of S^T = K Q^T:
   // lane (query lq, half hi), k-step kk -> Q[row][16*kk + 8*hi + 0..7].
@@ -117,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * D + 16 * kk + 8 * hi);
+    if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * sq + 16 * kk + 8 * hi);
     qf[kk] = x ^ qsign;  // sign flip for negative scale (exact)
   }
 
@@ -166,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
       const int r = R0 + lane / CH, p = lane % CH;
       const int cg = is_v ? (p ^ vswz(r)) : (p ^ (r % CH));
       const int grow = min(k0 + r, N - 1);
-      __builtin_amdgcn_global_load_lds(Xh + (size_t)grow * D + cg * 8,
+      __builtin_amdgcn_global_load_lds(Xh + (size_t)grow * skv + cg * 8,
                                        (lds_void*)(dst + R0 * ROWB), 16, 0, 0);
     }
   };
@@ -401,7 +451,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
   const float ltot = half_swap_sum(lsum);
   const float inv = 1.f / ltot;
   if (qi < N) {
-    uint16_t* orow = O + head + (size_t)qi * D;
+    uint16_t* orow = prm.o + qbase + (size_t)qi * sq;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -411,27 +461,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
         out[1] = TT::pack2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
         *(u32x2*)(orow + 32 * db + 8 * g4 + 4 * hi) = out;
       }
-    if (hi == 0) LSE[(size_t)bh * N + qi] = kLn2 * (mref + __log2f(ltot));
+    if (hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
   }
 }
 
 template <typename TT, int D>
 hipError_t launch_half(const FwdArgs& a) {
-  const int n_qtiles = (int)((a.N + kBM - 1) / kBM);
-  const int bh_count = (int)(a.B * a.H);
-  const int64_t grid = (int64_t)n_qtiles * bh_count;
-  const float c = fabsf(a.scale) * kLog2e;
-  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  FwdParams p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.o = (uint16_t*)a.o;
+  p.lse = a.lse;
+  p.cu = a.cu_seqlens;
+  p.seqlen = (int)a.N;  // dense N, or the longest packed sequence
+  p.total = (int)a.total;
+  p.heads = (int)a.H;
+  p.group = (int)(a.H / a.H_kv);
+  p.n_qtiles = (int)((a.N + kBM - 1) / kBM);
+  p.bh_count = (int)(a.B * a.H);
+  p.c = fabsf(a.scale) * kLog2e;
+  p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  const int64_t grid = (int64_t)p.n_qtiles * p.bh_count;
   if (a.causal)
     hipLaunchKernelGGL((fwd_kernel<TT, D, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, (int)a.N, n_qtiles, bh_count,
-                       c, qsign);
+                       a.stream, p);
   else
     hipLaunchKernelGGL((fwd_kernel<TT, D, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, (int)a.N, n_qtiles, bh_count,
-                       c, qsign);
+                       a.stream, p);
   return hipGetLastError();
 }
 

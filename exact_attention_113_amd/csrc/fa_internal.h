@@ -19,6 +19,12 @@ struct FwdArgs {
   int causal;
   int dtype;
   hipStream_t stream;
+  // Dense: B batches of N tokens each and H_kv = H. Packed variable-length
+  // batch: B sequences given by cu_seqlens (device memory), N = the longest
+  // sequence, total = tokens in the batch; H_kv divides H.
+  int64_t H_kv;
+  const int32_t* cu_seqlens;
+  int64_t total;
 };
 
 struct BwdArgs {

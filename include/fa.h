@@ -100,6 +100,41 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
                      int dtype, void* stream);
 
 /*
+ * fa_forward_varlen - fused attention forward over a packed batch of
+ * variable-length sequences, with grouped K/V heads (GQA/MQA).
+ *
+ * The variants named by "Flash Attention algorithm design and I/O
+ * optimisation" in its deployment and verification answers: variable-length
+ * batches and shared K/V heads. Sequence b is tokens [cu_seqlens[b],
+ * cu_seqlens[b+1]) of the packed tensors and attends only within itself (a
+ * causal query at position i of its sequence sees positions 0..i). Query
+ * head h reads K/V head h / (H / H_kv). Per (sequence, head) the result is
+ * that of fa_forward.
+ *
+ *   q, o        [total, H, D] of `dtype` (token-major, heads interleaved)
+ *   k, v        [total, H_kv, D] of `dtype`
+ *   lse         out [H, total] fp32, natural log
+ *   cu_seqlens  device memory, batch + 1 int32 offsets, caller-owned; the
+ *               caller guarantees 0 = cu[0] <= cu[1] <= ... <= cu[batch] =
+ *               total and cu[b+1] - cu[b] <= max_seqlen. Offsets outside
+ *               [0, total] are clamped and longer sequences truncated to
+ *               max_seqlen rows, so no access leaves the tensors; tokens not
+ *               covered by any sequence are not written.
+ *   batch       number of sequences (>= 1)
+ *   max_seqlen  longest sequence, 1 <= max_seqlen <= total
+ *   H, H_kv     query and K/V heads; H_kv divides H
+ *   D           64 or 128
+ *   scale, causal, stream  as for fa_forward
+ *   dtype       FA_FP16 or FA_BF16 (FA_FP32 returns FA_ERR_UNSUPPORTED)
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int64_t batch, int64_t max_seqlen,
+                            int64_t total, int64_t H, int64_t H_kv, int64_t D, float scale,
+                            int causal, int dtype, void* stream);
+
+/*
  * fa_backward_workspace_bytes - device workspace fa_backward needs for
  * this shape: two fp32 row statistics [B, H, N] (delta = rowsum(dO * O) and
  * LSE * log2(e)), each padded to 256 bytes (the two-phase workspace query of

@@ -18,6 +18,7 @@ Sources (pages cited by title and section):
 from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_online,
+    attention_forward_varlen,
     attention_backward,
     attention_probabilities,
 )

@@ -193,3 +193,40 @@ def attention_backward(q, k, v, do, scale, causal):
                 dq[b, h, r0:r1] = scale * (ds @ k[b, h])
                 dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])
     return dq, dk, dv
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens, scale, causal):
+    """Packed variable-length batch with grouped K/V heads (fp64).
+
+    The deployment variants named by the "Flash Attention algorithm design
+    and I/O optimisation" page (variable-length batches, shared K/V heads):
+    sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of the packed
+    tensors and attends only within itself; query head h reads K/V head
+    h // (H // H_kv). Each (sequence, head) is exact attention, computed by
+    attention_forward on that sequence's rows.
+
+    q: [total, H, D]; k, v: [total, H_kv, D]. Returns O [total, H, D] and
+    LSE [H, total]; tokens outside every sequence stay NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    total, H, D = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (total, H_kv, D) or v.shape != k.shape or H % H_kv != 0:
+        raise ValueError("need q [total, H, D] and k, v [total, H_kv, D] with H_kv | H")
+    group = H // H_kv
+    o = np.full((total, H, D), np.nan)
+    lse = np.full((H, total), np.nan)
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 <= s0:
+            continue
+        for h in range(H):
+            hk = h // group
+            ob, lb = attention_forward(q[None, None, s0:s1, h], k[None, None, s0:s1, hk],
+                                       v[None, None, s0:s1, hk], scale, causal)
+            o[s0:s1, h] = ob[0, 0]
+            lse[h, s0:s1] = lb[0, 0]
+    return o, lse

@@ -311,10 +311,70 @@ def pin_torch_autograd(orc):
             np.testing.assert_allclose(g, t.grad.numpy(), atol=1e-12, rtol=0)
 
 
+# ---------------------------------------------------------------- packed / grouped
+
+def brute_force_varlen(q, k, v, cu, scale, causal):
+    """Scalar loops over a packed batch: sequence b is tokens cu[b]..cu[b+1]-1,
+    query head h uses K/V head h // (H // H_kv). q: [total][H][D] nested lists."""
+    total, H, D = len(q), len(q[0]), len(q[0][0])
+    group = H // len(k[0])
+    o = [[[math.nan] * D for _ in range(H)] for _ in range(total)]
+    lse = [[math.nan] * total for _ in range(H)]
+    for b in range(len(cu) - 1):
+        for h in range(H):
+            hk = h // group
+            for i in range(cu[b], cu[b + 1]):
+                keys = range(cu[b], i + 1) if causal else range(cu[b], cu[b + 1])
+                s = [scale * sum(q[i][h][t] * k[j][hk][t] for t in range(D)) for j in keys]
+                m = max(s)
+                wts = [math.exp(x - m) for x in s]
+                tot = sum(wts)
+                for t in range(D):
+                    o[i][h][t] = sum(wt * v[j][hk][t] for wt, j in zip(wts, keys)) / tot
+                lse[h][i] = m + math.log(tot)
+    return o, lse
+
+
+def pin_varlen_brute_force(orc):
+    """Packed sequences with shared K/V heads against independent scalar loops
+    (lengths 3, 1, 0, 5; H = 4 over H_kv = 2, and MQA H_kv = 1)."""
+    cu = [0, 3, 4, 4, 9]
+    for H_kv in (2, 1):
+        q = _rand((9, 4, 3), 31)
+        k = _rand((9, H_kv, 3), 32)
+        v = _rand((9, H_kv, 3), 33)
+        for causal in (False, True):
+            o, lse = orc.attention_forward_varlen(q, k, v, cu, 0.7, causal)
+            bo, bl = brute_force_varlen(q.tolist(), k.tolist(), v.tolist(), cu, 0.7, causal)
+            np.testing.assert_allclose(o, np.array(bo), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-12)
+
+
+def pin_varlen_sequences_independent(orc):
+    """Changing the tokens of one sequence leaves every other sequence's
+    outputs unchanged, and reordering the sequences in the pack moves their
+    outputs with them."""
+    cu = [0, 5, 7, 13]
+    q, k, v = (_rand((13, 2, 4), s) for s in (41, 42, 43))
+    o, lse = orc.attention_forward_varlen(q, k, v, cu, 0.5, True)
+    k2 = k.copy()
+    k2[5:7] += _rand((2, 2, 4), 44)
+    o2, _ = orc.attention_forward_varlen(q, k2, v, cu, 0.5, True)
+    np.testing.assert_array_equal(o2[:5], o[:5])
+    np.testing.assert_array_equal(o2[7:], o[7:])
+    assert np.abs(o2[5:7] - o[5:7]).max() > 1e-3
+    perm = list(range(7, 13)) + list(range(0, 5)) + list(range(5, 7))
+    o3, lse3 = orc.attention_forward_varlen(q[perm], k[perm], v[perm], [0, 6, 11, 13], 0.5, True)
+    np.testing.assert_allclose(o3, o[perm], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse3, lse[:, perm], rtol=0, atol=1e-12)
+
+
+VARLEN_PINS = [pin_varlen_brute_force, pin_varlen_sequences_independent]
+
 FORWARD_PINS = [pin_golden_forward, pin_brute_force, pin_online_equals_three_pass,
                 pin_rows_sum_to_one, pin_constant_v, pin_causal_row0, pin_scale_zero,
                 pin_single_key, pin_permutations, pin_torch_sdpa, pin_row_chunking]
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_grad_sums,
                  pin_constant_v_grads, pin_scale_zero_grads, pin_delta_two_ways,
                  pin_torch_autograd]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS

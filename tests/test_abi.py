@@ -123,3 +123,30 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def fwd_varlen(q=A, k=A, v=A, o=A, lse=A, cu=A, batch=2, max_seqlen=8, total=16, H=4, H_kv=2,
+               D=64, scale=0.125, causal=1, dtype=2):
+    return _lib.load().fa_forward_varlen(q, k, v, o, lse, cu, batch, max_seqlen, total, H, H_kv,
+                                         D, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(v=A + 8), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(cu=A + 2), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H_kv=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H=6, H_kv=4), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(total=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen=17), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(D=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_forward_varlen_validation(kw, status):
+    assert fwd_varlen(**kw) == status
+    assert _lib.last_error() != ""

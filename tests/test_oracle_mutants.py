@@ -48,6 +48,10 @@ MUTANTS = {
                            "dq[b, h, r0:r1] = scale * (ds @ v[b, h])"),
     "bwd_dk_uses_grad": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
                          "dk[b, h] += scale * (ds.T @ g)"),
+    "varlen_head_map_mod": ("            hk = h // group\n            ob, lb",
+                            "            hk = h % H_kv\n            ob, lb"),
+    "varlen_sequence_shift": ("        s0, s1 = cu[b], cu[b + 1]\n        if s1 <= s0",
+                              "        s0, s1 = cu[b], cu[b + 1] + (1 if b == 0 else 0)\n        if s1 <= s0"),
     "bwd_dk_sign": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
                     "dk[b, h] -= scale * (ds.T @ q[b, h, r0:r1])"),
 }

@@ -100,6 +100,70 @@ def bf16_training():
                     True, 3, backward=True)
 
 
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of variable-length sequences with grouped K/V heads."""
+    name: str
+    lengths: tuple
+    H: int
+    H_kv: int
+    D: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    @property
+    def total(self):
+        return sum(self.lengths)
+
+    def cu_seqlens(self):
+        cu = [0]
+        for n in self.lengths:
+            cu.append(cu[-1] + n)
+        return cu
+
+    def flops_fwd(self):
+        """4 n^2 D per sequence and head, halved if causal."""
+        f = sum(4.0 * self.H * n * n * self.D for n in self.lengths)
+        return f / 2 if self.causal else f
+
+    def bytes_fwd(self):
+        esize = torch.empty((), dtype=self.torch_dtype).element_size()
+        t = self.total
+        return (2 * t * self.H + 2 * t * self.H_kv) * self.D * esize + 4 * t * self.H
+
+
+def varlen_gqa():
+    """16 causal bf16 sequences of 256..4096 tokens (seeded, uniform), 32 query
+    heads over 8 K/V heads, D = 128: a prefill batch with grouped-query
+    attention."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(4)
+    lengths = tuple(int(x) for x in torch.randint(256, 4097, (16,), generator=g))
+    return VarlenWorkload("bf16 causal varlen GQA 16 seqs 256..4096 H32/8 D128", lengths,
+                          32, 8, 128, "bf16", True, 4)
+
+
+def make_varlen_inputs(w: VarlenWorkload, device="cpu"):
+    """Packed q [total, H, D], k, v [total, H_kv, D] from one generator seeded
+    with w.seed (drawn in the order q, k, v), and cu_seqlens as int32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    q = torch.randn((w.total, w.H, w.D), generator=g).to(w.torch_dtype)
+    k = torch.randn((w.total, w.H_kv, w.D), generator=g).to(w.torch_dtype)
+    v = torch.randn((w.total, w.H_kv, w.D), generator=g).to(w.torch_dtype)
+    cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32)
+    return q.to(device), k.to(device), v.to(device), cu.to(device)
+
+
 def all_workloads():
     return [fp32_small(), bf16_short(), fp16_causal_4k()] + bf16_causal_sweep() + [
         bf16_training()]
