@@ -19,6 +19,8 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_online,
     attention_forward_varlen,
+    attention_decode,
+    merge_partials,
     attention_backward,
     attention_probabilities,
 )

@@ -230,3 +230,73 @@ def attention_forward_varlen(q, k, v, cu_seqlens, scale, causal):
             o[s0:s1, h] = ob[0, 0]
             lse[h, s0:s1] = lb[0, 0]
     return o, lse
+
+
+def attention_decode(q, k_cache, v_cache, cache_seqlens, scale):
+    """Attention of new tokens against a key/value cache (fp64).
+
+    The decode case of the "Flash Attention algorithm design and I/O
+    optimisation" page ("Training and inference value": each step brings
+    only new tokens but reads the whole, growing cache). Sequence b's cache
+    holds L_b = cache_seqlens[b] tokens, of which its s_q new tokens are the
+    last s_q; new token t (0-based) sits at position L_b - s_q + t and, by
+    the causal rule, sees cache keys 0 .. L_b - s_q + t. Query head h reads
+    K/V head h // (H // H_kv). A row that sees no key (L_b < s_q - t) gets
+    O = 0 and LSE = -inf. Each visible row is exact attention over its keys:
+    scores, max, exponentials, their sum, division, then P V.
+
+    q: [B, s_q, H, D]; k_cache, v_cache: [B, cap, H_kv, D]; cache_seqlens:
+    B integers in [0, cap]. Returns O [B, s_q, H, D] and LSE [B, H, s_q].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    B, s_q, H, D = q.shape
+    cap, H_kv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, cap, H_kv, D) or v_cache.shape != k_cache.shape or H % H_kv:
+        raise ValueError("need q [B, s_q, H, D] and caches [B, cap, H_kv, D] with H_kv | H")
+    group = H // H_kv
+    o = np.zeros((B, s_q, H, D))
+    lse = np.full((B, H, s_q), -np.inf)
+    for b in range(B):
+        L = int(cache_seqlens[b])
+        if not 0 <= L <= cap:
+            raise ValueError("cache_seqlens outside [0, cap]")
+        for t in range(s_q):
+            n = min(L, L - s_q + t + 1)  # keys 0 .. L - s_q + t
+            if n <= 0:
+                continue
+            for h in range(H):
+                hk = h // group
+                s = scale * (k_cache[b, :n, hk] @ q[b, t, h])
+                m = s.max()
+                e = np.exp(s - m)
+                l = e.sum()
+                o[b, t, h] = (e / l) @ v_cache[b, :n, hk]
+                lse[b, h, t] = m + np.log(l)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Exact attention over a union of disjoint key sets from the results
+    over each set: the rescale-and-add of the online softmax ("From
+    Self-Attention to FlashAttention", section 2) applied once per part.
+
+    With LSE_s = ln sum_{j in set s} exp(score_j) and O_s the attention over
+    set s, the whole has LSE = ln sum_s exp(LSE_s) and
+    O = sum_s exp(LSE_s - LSE) O_s. Parts with LSE_s = -inf (empty sets)
+    carry no weight; if every part is empty the result is O = 0, LSE = -inf.
+
+    o_parts: [S, ..., D]; lse_parts: [S, ...]. Returns (O [..., D], LSE [...]).
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    safe_m = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - safe_m)                   # exp(-inf) = 0 for empty parts
+    total = w.sum(axis=0)
+    lse = np.where(total > 0, safe_m + np.log(np.where(total > 0, total, 1.0)), -np.inf)
+    o = np.where((total > 0)[..., None],
+                 (w[..., None] * o_parts).sum(axis=0) / np.where(total > 0, total, 1.0)[..., None],
+                 0.0)
+    return o, lse

@@ -371,10 +371,105 @@ def pin_varlen_sequences_independent(orc):
 
 VARLEN_PINS = [pin_varlen_brute_force, pin_varlen_sequences_independent]
 
+def brute_force_decode(q, kc, vc, lens, scale):
+    """Scalar loops for decode: new token t of sequence b sits at position
+    L_b - s_q + t and sees cache keys 0 .. L_b - s_q + t; query head h uses
+    K/V head h // (H // H_kv); a row with no visible key is O = 0,
+    LSE = -inf. q: [B][s_q][H][D]; caches [B][cap][H_kv][D] nested lists."""
+    B, s_q, H, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    group = H // len(kc[0][0])
+    o = [[[[0.0] * D for _ in range(H)] for _ in range(s_q)] for _ in range(B)]
+    lse = [[[-math.inf] * s_q for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for t in range(s_q):
+            last = lens[b] - s_q + t  # last visible key position
+            keys = [j for j in range(lens[b]) if j <= last]
+            if not keys:
+                continue
+            for h in range(H):
+                hk = h // group
+                sc = [scale * sum(q[b][t][h][d] * kc[b][j][hk][d] for d in range(D)) for j in keys]
+                m = max(sc)
+                wts = [math.exp(x - m) for x in sc]
+                tot = sum(wts)
+                for d in range(D):
+                    o[b][t][h][d] = sum(wt * vc[b][j][hk][d] for wt, j in zip(wts, keys)) / tot
+                lse[b][h][t] = m + math.log(tot)
+    return o, lse
+
+
+def pin_decode_brute_force(orc):
+    """Decode against scalar loops: two sequences (cache lengths 5 and 1 of
+    capacity 6, two new tokens each, so one row of the second sees no key),
+    4 query heads over 2 K/V heads."""
+    q = _rand((2, 2, 4, 3), 51)
+    kc = _rand((2, 6, 2, 3), 52)
+    vc = _rand((2, 6, 2, 3), 53)
+    lens = [5, 1]
+    o, lse = orc.attention_decode(q, kc, vc, lens, 0.8)
+    bo, bl = brute_force_decode(q.tolist(), kc.tolist(), vc.tolist(), lens, 0.8)
+    np.testing.assert_allclose(o, np.array(bo), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(np.array(bl)))
+    fin = np.isfinite(np.array(bl))
+    np.testing.assert_allclose(lse[fin], np.array(bl)[fin], rtol=0, atol=1e-12)
+    assert np.isneginf(lse[1, :, 0]).all() and (o[1, 0] == 0).all()
+
+
+def pin_decode_is_causal_suffix(orc):
+    """Decoding the last s_q tokens of a sequence against its cache gives the
+    last s_q rows of the causal forward over the whole sequence (the forward
+    oracle is pinned on its own); cache slots past the length are ignored."""
+    L, cap, s_q, H, H_kv, D = 7, 10, 3, 4, 2, 5
+    qf = _rand((H, L, D), 61)
+    kf = _rand((H_kv, L, D), 62)
+    vf = _rand((H_kv, L, D), 63)
+    group = H // H_kv
+    ref_o, ref_l = orc.attention_forward(qf[None], np.repeat(kf, group, axis=0)[None],
+                                         np.repeat(vf, group, axis=0)[None], 0.6, True)
+    kc = np.full((1, cap, H_kv, D), 1e6)
+    vc = np.full((1, cap, H_kv, D), -1e6)
+    kc[0, :L] = kf.transpose(1, 0, 2)
+    vc[0, :L] = vf.transpose(1, 0, 2)
+    q = qf[:, L - s_q:].transpose(1, 0, 2)[None]
+    o, lse = orc.attention_decode(q, kc, vc, [L], 0.6)
+    np.testing.assert_allclose(o[0], ref_o[0, :, L - s_q:].transpose(1, 0, 2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], ref_l[0, :, L - s_q:], rtol=0, atol=1e-12)
+
+
+def pin_merge_partials(orc):
+    """Attention over all keys equals the merge of attention over disjoint
+    key subsets (one of them empty), in any order; all-empty gives O = 0,
+    LSE = -inf."""
+    q = _rand((1, 1, 3, 4), 71)
+    k = _rand((1, 1, 11, 4), 72)
+    v = _rand((1, 1, 11, 4), 73)
+    whole_o, whole_l = orc.attention_forward(
+        np.concatenate([q, np.zeros((1, 1, 8, 4))], axis=2), k, v, 0.9, False)
+    parts = [[0, 4, 9], [1, 2, 3, 10], [5, 6, 7, 8]]
+    os_, ls_ = [], []
+    for idx in parts:
+        po, pl = orc.attention_forward(
+            np.concatenate([q, np.zeros((1, 1, len(idx) - 3, 4))], axis=2) if len(idx) > 3 else q,
+            k[:, :, idx], v[:, :, idx], 0.9, False)
+        os_.append(po[0, 0, :3])
+        ls_.append(pl[0, 0, :3])
+    os_.append(np.zeros((3, 4)))
+    ls_.append(np.full(3, -np.inf))
+    for order in ([0, 1, 2, 3], [3, 2, 0, 1]):
+        o, l = orc.merge_partials(np.stack([os_[i] for i in order]), np.stack([ls_[i] for i in order]))
+        np.testing.assert_allclose(o, whole_o[0, 0, :3], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, whole_l[0, 0, :3], rtol=0, atol=1e-12)
+    o, l = orc.merge_partials(np.zeros((2, 3, 4)), np.full((2, 3), -np.inf))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+DECODE_PINS = [pin_decode_brute_force, pin_decode_is_causal_suffix, pin_merge_partials]
+
+
 FORWARD_PINS = [pin_golden_forward, pin_brute_force, pin_online_equals_three_pass,
                 pin_rows_sum_to_one, pin_constant_v, pin_causal_row0, pin_scale_zero,
                 pin_single_key, pin_permutations, pin_torch_sdpa, pin_row_chunking]
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_grad_sums,
                  pin_constant_v_grads, pin_scale_zero_grads, pin_delta_two_ways,
                  pin_torch_autograd]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS + DECODE_PINS

@@ -52,6 +52,12 @@ MUTANTS = {
                             "            hk = h % H_kv\n            ob, lb"),
     "varlen_sequence_shift": ("        s0, s1 = cu[b], cu[b + 1]\n        if s1 <= s0",
                               "        s0, s1 = cu[b], cu[b + 1] + (1 if b == 0 else 0)\n        if s1 <= s0"),
+    "decode_causal_off_by_one": ("n = min(L, L - s_q + t + 1)", "n = min(L, L - s_q + t)"),
+    "decode_ignores_length": ("n = min(L, L - s_q + t + 1)", "n = min(cap, cap - s_q + t + 1)"),
+    "decode_head_map_mod": ("                hk = h // group\n                s = scale",
+                            "                hk = h % H_kv\n                s = scale"),
+    "merge_unweighted": ("(w[..., None] * o_parts).sum(axis=0)", "o_parts.sum(axis=0)"),
+    "merge_lse_drops_max": ("safe_m + np.log(", "np.log("),
     "bwd_dk_sign": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
                     "dk[b, h] -= scale * (ds.T @ q[b, h, r0:r1])"),
 }
