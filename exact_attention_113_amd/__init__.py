@@ -106,6 +106,57 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, ou
     return out, lse
 
 
+def decode_workspace_bytes(batch, s_q, H, H_kv, max_seqlen_k, D):
+    return int(_lib.load().fa_decode_workspace_bytes(batch, s_q, H, H_kv, max_seqlen_k, D))
+
+
+def decode(q, k_cache, v_cache, cache_seqlens, max_seqlen_k=None, scale=None, out=None, lse=None,
+           workspace=None):
+    """Attention of s_q new tokens per sequence against a key/value cache.
+
+    q: [B, s_q, H, D]; k_cache, v_cache: [B, cap, H_kv, D]; cache_seqlens: int32 [B]
+    on q's device (cached tokens per sequence, the new ones included as the
+    last s_q). New token t sees keys 0 .. L_b - s_q + t. max_seqlen_k bounds the
+    lengths (default: cap). Returns (o [B, s_q, H, D], lse fp32 [B, H, s_q]).
+    """
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape or \
+            q.shape[0] != k_cache.shape[0] or q.shape[3] != k_cache.shape[3]:
+        raise ValueError(f"need q [B, s_q, H, D] and caches [B, cap, H_kv, D], got "
+                         f"{tuple(q.shape)}, {tuple(k_cache.shape)}, {tuple(v_cache.shape)}")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or \
+            v_cache.dtype != q.dtype:
+        raise TypeError("dtype must be float16 or bfloat16 (all equal)")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("cache_seqlens", cache_seqlens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, s_q, H, D = q.shape
+    cap, H_kv = k_cache.shape[1], k_cache.shape[2]
+    if cache_seqlens.dtype != torch.int32 or cache_seqlens.shape != (B,):
+        raise ValueError("cache_seqlens must be int32 [B]")
+    if max_seqlen_k is None:
+        max_seqlen_k = cap
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, s_q, H, H_kv, max_seqlen_k, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           cache_seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(), ws_ptr,
+                           ws_len, B, s_q, cap, int(max_seqlen_k), H, H_kv, D, float(scale),
+                           _DTYPES[q.dtype], _stream_handle(q))
+    _lib.check("fa_decode", st)
+    return out, lse
+
+
 def backward_workspace_bytes(B, H, N, D):
     return int(_lib.load().fa_backward_workspace_bytes(B, H, N, D))
 

@@ -16,6 +16,9 @@ PROTOTYPES = {
     "fa_forward_varlen": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                          _I64, _F, _I, _I, _P]),
     "fa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "fa_decode_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64]),
+    "fa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64,
+                                 _I64, _I64, _F, _I, _P]),
     "fa_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64,
                                    _I64, _I64, _F, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),

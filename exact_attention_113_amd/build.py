@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_decode.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -197,3 +197,75 @@ const char* fa_status_string(int status) {
 const char* fa_last_error(void) { return g_last_error; }
 
 }  // extern "C"
+
+namespace {
+
+// Checks shared by the decode size query and the decode call.
+fa_status check_decode(int64_t B, int64_t s_q, int64_t cap, int64_t max_seqlen_k, int64_t H,
+                       int64_t H_kv, int64_t D, float scale, int dtype, const char* who) {
+  if (B < 1 || s_q < 1 || cap < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: need batch, s_q, cache_capacity >= 1", who);
+  if (max_seqlen_k < 0 || max_seqlen_k > cap)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: need 0 <= max_seqlen_k (%lld) <= capacity (%lld)",
+                who, (long long)max_seqlen_k, (long long)cap);
+  if (H_kv < 1 || H < 1 || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: H (%lld) must be a positive multiple of H_kv (%lld)",
+                who, (long long)H, (long long)H_kv);
+  fa_status s = check_shape(B, H, cap, D, scale, dtype);
+  if (s != FA_OK) return s;
+  int64_t qelems = 0;
+  if (__builtin_mul_overflow(B * H, s_q, &qelems) || __builtin_mul_overflow(qelems, D * 4, &qelems))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: B*s_q*H*D overflows", who);
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: fp32 is not supported", who);
+  if ((H / H_kv) * s_q > 32)
+    return fail(FA_ERR_UNSUPPORTED,
+                "%s: (H / H_kv) * s_q = %lld rows per K/V head; at most 32 are supported", who,
+                (long long)((H / H_kv) * s_q));
+  if (cap > (int64_t)1 << 30 || B * H_kv * fa::kMaxSplits > (int64_t)0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "%s: sizes exceed one grid", who);
+  return FA_OK;
+}
+
+}  // namespace
+
+size_t fa_decode_workspace_bytes(int64_t batch, int64_t s_q, int64_t H, int64_t H_kv,
+                                 int64_t max_seqlen_k, int64_t D) {
+  fa::DecodePlan plan;
+  if (!fa::decode_plan(batch, s_q, H, H_kv, max_seqlen_k, D, &plan)) return 0;
+  return plan.total;
+}
+
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* cache_seqlens, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, int64_t batch, int64_t s_q, int64_t cache_capacity,
+                    int64_t max_seqlen_k, int64_t H, int64_t H_kv, int64_t D, float scale,
+                    int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_decode: q, k_cache, v_cache, cache_seqlens, o and lse must be non-NULL");
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(o, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: q, caches and o must be 16-byte aligned");
+  if (misaligned(lse, 4) || misaligned(cache_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: lse and cache_seqlens must be 4-byte aligned");
+  fa_status s = check_decode(batch, s_q, cache_capacity, max_seqlen_k, H, H_kv, D, scale, dtype,
+                             "fa_decode");
+  if (s != FA_OK) return s;
+  fa::DecodePlan plan;
+  if (!fa::decode_plan(batch, s_q, H, H_kv, max_seqlen_k, D, &plan))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode: no plan for these sizes");
+  if (plan.total > 0) {
+    if (!workspace)
+      return fail(FA_ERR_WORKSPACE, "fa_decode: workspace is NULL (needs %lld bytes)",
+                  (long long)plan.total);
+    if (workspace_bytes < plan.total)
+      return fail(FA_ERR_WORKSPACE, "fa_decode: workspace too small (needs %lld bytes)",
+                  (long long)plan.total);
+    if (misaligned(workspace, 256))
+      return fail(FA_ERR_WORKSPACE, "fa_decode: workspace must be 256-byte aligned");
+  }
+  fa::DecodeArgs a{q,     k_cache,        v_cache, cache_seqlens, o, lse, workspace,
+                   batch, s_q,            cache_capacity, max_seqlen_k, H, H_kv, D,
+                   scale, dtype, (hipStream_t)stream};
+  return hip_status(fa::launch_decode(a, plan), "fa_decode");
+}

@@ -1,0 +1,440 @@
+// Attention of a few new tokens against a key/value cache (decode), bf16 /
+// fp16 on gfx950.
+//
+// Each step of token-by-token generation brings only the new tokens' queries
+// but reads the whole, growing cache ("Flash Attention algorithm design and
+// I/O optimisation", "Training and inference value"), so the work is bound
+// by streaming K and V from HBM once. New token t of a sequence with L cached
+// tokens sits at position L - s_q + t and sees cache keys 0 .. L - s_q + t.
+//
+// Work split (split-KV). One workgroup takes one (sequence, K/V head, key
+// chunk): all query heads of the group sharing that K/V head and all s_q new
+// tokens become the rows of one 32-row MFMA tile, so every K/V byte is read
+// once per step. Its four waves take every fourth 32-key block of the chunk
+// and keep their own online-softmax state (running maximum, running sum,
+// fp32 accumulator: "From Self-Attention to FlashAttention", section 2); each
+// wave streams its blocks through its own double-buffered LDS region with
+// direct global->LDS loads, so the key loop needs no workgroup barrier. At
+// the end the four partial states are merged through LDS with the same
+// rescale-and-add, and the chunk's (O, LSE) is written: straight to the
+// output when the cache is one chunk, else to a workspace that
+// decode_merge_kernel combines over the chunks by LSE.
+//
+// Products and layouts follow the forward kernel: S^T = K Q^T and
+// O^T = V^T P^T on 32x32x16 MFMAs, K rows with an XOR chunk swizzle, V read
+// transposed from LDS with ds_read_b64_tr_b16.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDKB = 32;  // keys per block
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+struct DecParams {
+  const uint16_t* q;        // [B, s_q, H, D]
+  const uint16_t* k;        // [B, cap, H_kv, D]
+  const uint16_t* v;        // [B, cap, H_kv, D]
+  uint16_t* o;              // [B, s_q, H, D]
+  float* lse;               // [B, H, s_q]
+  const int32_t* seqlens;   // [B] cached tokens per sequence
+  float* part_o;            // [B, H, s_q, n_splits, D] (split mode)
+  float* part_lse;          // [B, H, s_q, n_splits]    (split mode)
+  int s_q, cap, max_len, heads, hkv, group, n_splits, chunk;
+  float c;                  // |scale| * log2(e)
+  uint32_t qsign;           // sign flip of Q for a negative scale
+};
+
+template <typename TT, int D>
+__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams prm) {
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int ROWB = 2 * D;              // bytes per row
+  constexpr int BLKB = kDKB * ROWB;        // bytes of one K or V block
+  constexpr int RPI = 64 / CH;             // rows per wave-wide direct load
+  constexpr int LPB = kDKB / RPI;          // direct loads per block and tensor
+  constexpr int DB = D / 32;               // 32-row blocks of the head dim
+  constexpr int KK = D / 16;               // k-steps of the score MFMA
+  constexpr int OC = D / 4;                // 16-byte chunks of an fp32 output row
+  static_assert(kDecWaves * 2 * BLKB >= kDecWaves * 32 * D * 4, "merge buffer too small");
+  // Per wave: K block then V block, one region per buffer.
+  __shared__ __attribute__((aligned(1024))) char buf0[kDecWaves * 2 * BLKB];
+  __shared__ __attribute__((aligned(1024))) char buf1[kDecWaves * 2 * BLKB];
+  __shared__ float stat_m[kDecWaves][32];
+  __shared__ float stat_l[kDecWaves][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hi = lane >> 5;
+
+  int lin = blockIdx.x;
+  const int split = lin % prm.n_splits;
+  lin /= prm.n_splits;
+  const int hk = lin % prm.hkv;
+  const int b = lin / prm.hkv;
+  const int L = min(max(prm.seqlens[b], 0), prm.max_len);
+  const int k_lo = split * prm.chunk;
+  const int k_hi = min(L, k_lo + prm.chunk);
+  const int nblk = k_hi > k_lo ? (k_hi - k_lo + kDKB - 1) / kDKB : 0;
+  const int rows = prm.group * prm.s_q;
+
+  // Row lq of the tile: query head hk * group + lq / s_q, new token lq % s_q.
+  const int gq = lq / prm.s_q, tq = lq - gq * prm.s_q;
+  const int h = hk * prm.group + gq;
+  const bool row_ok = lq < rows;
+  // Keys visible to this row within the chunk: [k_lo, lim).
+  const int lim = min(min(L, L - prm.s_q + tq + 1), k_hi);
+
+  u32x4 qf[KK];
+  {
+    const uint16_t* qrow = prm.q + ((size_t)(b * prm.s_q + tq) * prm.heads + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row_ok) x = *(const u32x4*)(qrow + 16 * kk + 8 * hi);
+      qf[kk] = x ^ prm.qsign;
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float mrun = -INFINITY;  // running maximum, log2 units
+  float lsum = 0.f;        // this lane's share of the running sum
+
+  const size_t kv_stride = (size_t)prm.hkv * D;  // elements between cache rows
+  const uint16_t* Kb = prm.k + ((size_t)b * prm.cap * prm.hkv + hk) * D;
+  const uint16_t* Vb = prm.v + ((size_t)b * prm.cap * prm.hkv + hk) * D;
+
+  auto vswz = [](int r) __attribute__((always_inline)) {
+    return CH == 16 ? 4 * (r & 3) : 2 * (r & 3);
+  };
+  // Direct loads of block j's 32 K rows and 32 V rows into this wave's
+  // region; rows past the cache length repeat its last row (masked).
+  auto load_block = [&](int j, char* kdst, char* vdst) __attribute__((always_inline)) {
+    const int key0 = k_lo + kDKB * j;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      const int R0 = i * RPI;
+      const int r = R0 + lane / CH, p = lane % CH;
+      const size_t grow = (size_t)min(key0 + r, L - 1) * kv_stride;
+      const void* ksrc = Kb + grow + (p ^ (r % CH)) * 8;
+      const void* vsrc = Vb + grow + (p ^ vswz(r)) * 8;
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + R0 * ROWB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + R0 * ROWB), 16, 0, 0);
+    }
+  };
+
+  const int kxor = lq % CH;
+  const int koff = lq * ROWB;
+  const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1;
+  const int vlane = (4 * hi + tj) * ROWB + 8 * (tm & 1);
+  const int vx = (2 * dsub + (tm >> 1)) ^ vswz(tj);
+
+  // One 32-key block: scores, masked online softmax, P V.
+  auto compute_block = [&](int j, const char* kt, const char* vt) __attribute__((always_inline)) {
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 a = *(const u32x4*)(kt + koff + 16 * ((2 * kk + hi) ^ kxor));
+      s = TT::mma(a, qf[kk], s);
+    }
+    const int key0 = k_lo + kDKB * j;
+    uint32_t okm = 0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const bool ok = key < lim;
+      okm |= ok ? (1u << r) : 0u;
+      mx = ok ? fmaxf(mx, s[r]) : mx;
+    }
+    mx = half_swap_max(mx);
+    const float tmx = mx == -INFINITY ? -INFINITY : mx * prm.c;
+    const float mnew = fmaxf(mrun, tmx);
+    // Nothing visible yet: keep alpha = 1 (the state is still empty).
+    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
+    const float nm = -mnew;
+    float p[16];
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = fast_exp2(fmaf(s[r], prm.c, nm));
+      p[r] = ((okm >> r) & 1u) ? x : 0.f;
+      sum += p[r];
+    }
+    lsum = fmaf(lsum, alpha, sum);
+    mrun = mnew;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    u32x4 pf[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pf[hh][e] = TT::pack2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* base = vt + vlane + 16 * hh * ROWB + 16 * ((4 * db) ^ vx);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 u2 = __builtin_bit_cast(u32x2, up);
+        const u32x4 a = {l2[0], l2[1], u2[0], u2[1]};
+        oacc[db] = TT::mma(a, pf[hh], oacc[db]);
+      }
+  };
+
+  // This wave's blocks w, w + 4, ...: block i of the wave in buffer i % 2,
+  // the next one loading while the current one is computed. A wave reads
+  // only what it loaded itself, so its own vmcnt wait is the only sync.
+  char* k0 = buf0 + w * 2 * BLKB;
+  char* v0 = k0 + BLKB;
+  char* k1 = buf1 + w * 2 * BLKB;
+  char* v1 = k1 + BLKB;
+  const int ni = nblk > w ? (nblk - w + kDecWaves - 1) / kDecWaves : 0;
+  if (ni > 0) load_block(w, k0, v0);
+  for (int i = 0; i < ni; i += 2) {
+    if (i + 1 < ni) {
+      load_block(w + kDecWaves * (i + 1), k1, v1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPB) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    compute_block(w + kDecWaves * i, k0, v0);
+    if (i + 1 < ni) {
+      if (i + 2 < ni) {
+        load_block(w + kDecWaves * (i + 2), k0, v0);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPB) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute_block(w + kDecWaves * (i + 1), k1, v1);
+    }
+  }
+
+  // Merge the four waves' states: maximum M over the waves, each wave's
+  // weight 2^(m_w - M) (0 for a wave that saw no key), total sum, and the
+  // weighted accumulators summed through LDS.
+  const float lrow = half_swap_sum(lsum);
+  __syncthreads();  // every wave is done with its LDS blocks
+  if (hi == 0) {
+    stat_m[w][lq] = mrun;
+    stat_l[w][lq] = lrow;
+  }
+  __syncthreads();
+  auto row_stats = [&](int row, float& M, float& Ltot) __attribute__((always_inline)) {
+    M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x) M = fmaxf(M, stat_m[x][row]);
+    Ltot = 0.f;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x)
+      Ltot += stat_m[x][row] == -INFINITY ? 0.f : fast_exp2(stat_m[x][row] - M) * stat_l[x][row];
+  };
+  {
+    float M, Ltot;
+    row_stats(lq, M, Ltot);
+    const float f = mrun == -INFINITY ? 0.f : fast_exp2(mrun - M);
+    // Row lq of wave w's slab, 16-byte chunk c stored at c ^ (lq % OC) so
+    // that the 32 rows written together spread over the banks.
+    float* ob = (float*)buf0 + (size_t)(w * 32 + lq) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * g4 + e] * f;
+        const int cidx = 8 * db + 2 * g4 + hi;
+        *(f32x4*)(ob + 4 * (cidx ^ (lq % OC))) = x;
+      }
+  }
+  __syncthreads();
+  {
+    constexpr int SEG = D / 8;  // output elements per thread
+    const int row = tid >> 3, d0 = (tid & 7) * SEG;
+    if (row < rows) {
+      float M, Ltot;
+      row_stats(row, M, Ltot);
+      const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+      float acc[SEG];
+#pragma unroll
+      for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int x = 0; x < kDecWaves; ++x) {
+        const float* src = (const float*)buf0 + (size_t)(x * 32 + row) * D;
+#pragma unroll
+        for (int e = 0; e < SEG; e += 4) {
+          const f32x4 y = *(const f32x4*)(src + 4 * (((d0 + e) / 4) ^ (row % OC)));
+          acc[e] += y[0];
+          acc[e + 1] += y[1];
+          acc[e + 2] += y[2];
+          acc[e + 3] += y[3];
+        }
+      }
+      const int rg = row / prm.s_q, rt = row - rg * prm.s_q;
+      const int rh = hk * prm.group + rg;
+      const float lse_row = Ltot > 0.f ? kLn2 * (M + __log2f(Ltot)) : -INFINITY;
+      if (prm.n_splits == 1) {
+        uint16_t* orow = prm.o + ((size_t)(b * prm.s_q + rt) * prm.heads + rh) * D + d0;
+#pragma unroll
+        for (int e = 0; e < SEG; e += 8) {
+          u32x4 out;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) out[u] = TT::pack2(acc[e + 2 * u] * inv, acc[e + 2 * u + 1] * inv);
+          *(u32x4*)(orow + e) = out;
+        }
+        if ((tid & 7) == 0) prm.lse[((size_t)b * prm.heads + rh) * prm.s_q + rt] = lse_row;
+      } else {
+        const size_t prow = ((size_t)(b * prm.heads + rh) * prm.s_q + rt) * prm.n_splits + split;
+        float* po = prm.part_o + prow * D + d0;
+#pragma unroll
+        for (int e = 0; e < SEG; e += 4) {
+          f32x4 y = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+          *(f32x4*)(po + e) = y;
+        }
+        if ((tid & 7) == 0) prm.part_lse[prow] = lse_row;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Combine the chunks of one output row (b, h, t), one wave per row:
+// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s; chunks with
+// LSE_s = -inf carry no weight, and a row with none left is O = 0,
+// LSE = -inf.
+template <typename TT, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse,
+                                                           uint16_t* __restrict__ o,
+                                                           float* __restrict__ lse, int n_rows,
+                                                           int n_splits, int heads, int s_q) {
+  constexpr int PER = D / 64;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const float* pl = part_lse + (size_t)row * n_splits;
+  float m = -INFINITY;
+  for (int s = lane; s < n_splits; s += 64) m = fmaxf(m, pl[s]);
+  m = wave_max(m);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float ls = pl[s];
+      const float wt = ls == -INFINITY ? 0.f : __expf(ls - m);
+      wsum += wt;
+      const float* src = part_o + ((size_t)row * n_splits + s) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, src[e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int t = row % s_q, bh = row / s_q;
+  const int b = bh / heads, h = bh - b * heads;
+  uint16_t* dst = o + ((size_t)(b * s_q + t) * heads + h) * D + lane * PER;
+  if (PER == 2) {
+    *(uint32_t*)dst = TT::pack2(acc[0] * inv, acc[PER - 1] * inv);
+  } else {
+    const uint32_t x = TT::pack2(acc[0] * inv, 0.f);
+    *dst = (uint16_t)(x & 0xffffu);
+  }
+  if (lane == 0) lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
+template <typename TT, int D>
+hipError_t launch_typed(const DecodeArgs& a, const DecodePlan& plan) {
+  DecParams p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k_cache;
+  p.v = (const uint16_t*)a.v_cache;
+  p.o = (uint16_t*)a.o;
+  p.lse = a.lse;
+  p.seqlens = a.cache_seqlens;
+  p.part_o = plan.n_splits > 1 ? (float*)((char*)a.workspace + plan.part_o_off) : nullptr;
+  p.part_lse = plan.n_splits > 1 ? (float*)((char*)a.workspace + plan.part_lse_off) : nullptr;
+  p.s_q = (int)a.s_q;
+  p.cap = (int)a.cap;
+  p.max_len = (int)a.max_len;
+  p.heads = (int)a.H;
+  p.hkv = (int)a.H_kv;
+  p.group = (int)(a.H / a.H_kv);
+  p.n_splits = plan.n_splits;
+  p.chunk = plan.chunk;
+  p.c = fabsf(a.scale) * kLog2e;
+  p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  const int64_t grid = a.B * a.H_kv * plan.n_splits;
+  hipLaunchKernelGGL((decode_kernel<TT, D>), dim3((unsigned)grid), dim3(kDecThreads), 0, a.stream,
+                     p);
+  if (plan.n_splits > 1) {
+    const int n_rows = (int)(a.B * a.H * a.s_q);
+    hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((unsigned)((n_rows + 3) / 4)), dim3(256),
+                       0, a.stream, p.part_o, p.part_lse, p.o, p.lse, n_rows, plan.n_splits,
+                       p.heads, p.s_q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_plan(int64_t B, int64_t s_q, int64_t H, int64_t H_kv, int64_t max_len, int64_t D,
+                 DecodePlan* plan) {
+  if (B < 1 || s_q < 1 || H < 1 || H_kv < 1 || max_len < 0 || D < 1) return false;
+  // Enough workgroups to fill the chip a few times over, chunks of at least
+  // 128 keys (one block per wave), at most kMaxSplits chunks per row.
+  const int64_t units = B * H_kv;
+  const int64_t want = (kDecodeTargetWgs + units - 1) / units;
+  const int64_t most = max_len > 0 ? (max_len + 127) / 128 : 1;
+  int64_t n = want < most ? want : most;
+  if (n > kMaxSplits) n = kMaxSplits;
+  if (n < 1) n = 1;
+  int64_t chunk = max_len > 0 ? (max_len + n - 1) / n : 128;
+  chunk = (chunk + 127) / 128 * 128;
+  n = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
+  plan->n_splits = (int)n;
+  plan->chunk = (int)chunk;
+  auto pad = [](size_t x) { return (x + 255) / 256 * 256; };
+  if (n > 1) {
+    const size_t rows = (size_t)B * H * s_q;
+    plan->part_o_off = 0;
+    plan->part_o_bytes = pad(rows * n * D * 4);
+    plan->part_lse_off = plan->part_o_bytes;
+    plan->part_lse_bytes = pad(rows * n * 4);
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes;
+  } else {
+    plan->part_o_off = plan->part_o_bytes = plan->part_lse_off = plan->part_lse_bytes = 0;
+    plan->total = 0;
+  }
+  return true;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan) {
+  const bool bf = a.dtype == FA_BF16;
+  if (a.D == 128) return bf ? launch_typed<Bf16, 128>(a, plan) : launch_typed<F16, 128>(a, plan);
+  return bf ? launch_typed<Bf16, 64>(a, plan) : launch_typed<F16, 64>(a, plan);
+}
+
+}  // namespace fa

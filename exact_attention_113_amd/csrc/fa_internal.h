@@ -53,8 +53,37 @@ struct BwdWorkspace {
 };
 bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWorkspace* ws);
 
+// Decode: s_q new tokens per sequence against a K/V cache of capacity cap.
+struct DecodeArgs {
+  const void* q;             // [B, s_q, H, D]
+  const void* k_cache;       // [B, cap, H_kv, D]
+  const void* v_cache;       // [B, cap, H_kv, D]
+  const int32_t* cache_seqlens;  // [B], device
+  void* o;                   // [B, s_q, H, D]
+  float* lse;                // [B, H, s_q]
+  void* workspace;
+  int64_t B, s_q, cap, max_len, H, H_kv, D;
+  float scale;
+  int dtype;
+  hipStream_t stream;
+};
+
+// How the cache is cut into chunks (one workgroup per sequence, K/V head and
+// chunk) and where the per-chunk partial results go in the workspace.
+constexpr int64_t kDecodeTargetWgs = 2048;
+constexpr int64_t kMaxSplits = 64;
+struct DecodePlan {
+  int n_splits, chunk;
+  size_t part_o_off, part_o_bytes;      // fp32 [B, H, s_q, n_splits, D]
+  size_t part_lse_off, part_lse_bytes;  // fp32 [B, H, s_q, n_splits]
+  size_t total;                         // 0 when the cache is one chunk
+};
+bool decode_plan(int64_t B, int64_t s_q, int64_t H, int64_t H_kv, int64_t max_len, int64_t D,
+                 DecodePlan* plan);
+
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a, const BwdWorkspace& ws);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan);
 
 }  // namespace fa

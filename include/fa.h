@@ -179,6 +179,57 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       int64_t N, int64_t D, float scale, int causal, int dtype,
                       void* stream);
 
+/*
+ * fa_decode_workspace_bytes - device workspace fa_decode needs for these
+ * sizes: per-chunk partial results (fp32 O and LSE of every output row for
+ * every key chunk) when the cache is cut into more than one chunk, else 0.
+ * Same arguments as fa_decode. Returns 0 also for invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int64_t batch, int64_t s_q, int64_t H, int64_t H_kv,
+                                 int64_t max_seqlen_k, int64_t D);
+
+/*
+ * fa_decode - attention of new tokens against a key/value cache.
+ *
+ * The decode step of "Flash Attention algorithm design and I/O
+ * optimisation" ("Training and inference value"): each step brings s_q new
+ * tokens per sequence and reads the whole cache. Sequence b's cache holds
+ * L_b = cache_seqlens[b] tokens, its new tokens being the last s_q of them;
+ * new token t sees cache keys 0 .. L_b - s_q + t (causal), query head h reads
+ * K/V head h / (H / H_kv). A row that sees no key gets O = 0 and
+ * LSE = -inf. The cache is cut into chunks whose (O, LSE) results are merged
+ * exactly by LSE (the online-softmax rescale of "From Self-Attention to
+ * FlashAttention", section 2, applied to whole chunks).
+ *
+ *   q              [batch, s_q, H, D] of `dtype`
+ *   k_cache, v_cache  [batch, cache_capacity, H_kv, D] of `dtype`
+ *   cache_seqlens  device memory, batch int32 lengths, caller-owned; values
+ *                  are clamped into [0, max_seqlen_k], so no access leaves
+ *                  the caches
+ *   o              out [batch, s_q, H, D] of `dtype`
+ *   lse            out [batch, H, s_q] fp32, natural log
+ *   workspace      device scratch of fa_decode_workspace_bytes(...) bytes,
+ *                  256-byte aligned, caller-owned (may be NULL when that
+ *                  size is 0); contents on entry ignored, on return
+ *                  unspecified
+ *   max_seqlen_k   upper bound of cache_seqlens used to cut the chunks,
+ *                  0 <= max_seqlen_k <= cache_capacity
+ *   H, H_kv        query and K/V heads; H_kv divides H and
+ *                  (H / H_kv) * s_q <= 32 (else FA_ERR_UNSUPPORTED)
+ *   D              64 or 128
+ *   scale          any finite value (1/sqrt(D) is usual)
+ *   dtype          FA_FP16 or FA_BF16 (FA_FP32 returns FA_ERR_UNSUPPORTED)
+ *   stream         hipStream_t as void*; asynchronous, no allocation
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED,
+ * FA_ERR_WORKSPACE or FA_ERR_HIP.
+ */
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* cache_seqlens, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, int64_t batch, int64_t s_q, int64_t cache_capacity,
+                    int64_t max_seqlen_k, int64_t H, int64_t H_kv, int64_t D, float scale,
+                    int dtype, void* stream);
+
 /* fa_status_string - static, never-NULL name of a status code. */
 const char* fa_status_string(int status);
 

@@ -150,3 +150,48 @@ def fwd_varlen(q=A, k=A, v=A, o=A, lse=A, cu=A, batch=2, max_seqlen=8, total=16,
 def test_forward_varlen_validation(kw, status):
     assert fwd_varlen(**kw) == status
     assert _lib.last_error() != ""
+
+
+def dec(q=A, k=A, v=A, lens=A, o=A, lse=A, ws=A, ws_bytes=1 << 30, batch=2, s_q=1, cap=64,
+        max_len=64, H=8, H_kv=2, D=128, scale=0.125, dtype=2):
+    return _lib.load().fa_decode(q, k, v, lens, o, lse, ws, ws_bytes, batch, s_q, cap, max_len,
+                                 H, H_kv, D, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(lens=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(k=A + 8), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(lse=A + 2), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(s_q=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(cap=0, max_len=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_len=65), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_len=-1), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H=6, H_kv=4), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=9), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(D=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(H=64, H_kv=1), _lib.FA_ERR_UNSUPPORTED),
+    (dict(s_q=9, H=8, H_kv=2), _lib.FA_ERR_UNSUPPORTED),
+    (dict(ws=None, cap=4096, max_len=4096), _lib.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16, cap=4096, max_len=4096), _lib.FA_ERR_WORKSPACE),
+    (dict(ws=A + 16, cap=4096, max_len=4096), _lib.FA_ERR_WORKSPACE),
+])
+def test_decode_validation(kw, status):
+    assert dec(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_decode_workspace_size():
+    lib = _lib.load()
+    # One chunk (a short cache): no workspace.
+    assert lib.fa_decode_workspace_bytes(2, 1, 8, 2, 64, 128) == 0
+    # Several chunks: fp32 O and LSE per (row, chunk), each part 256-byte padded.
+    n = lib.fa_decode_workspace_bytes(2, 1, 8, 2, 4096, 128)
+    assert n > 0 and n % 256 == 0
+    rows = 2 * 8 * 1
+    splits = (n // 4 - 0) // (rows * 129)  # upper bound on the chunk count
+    assert 2 <= splits <= 64
+    assert lib.fa_decode_workspace_bytes(0, 1, 8, 2, 64, 128) == 0

@@ -1,0 +1,108 @@
+"""Decode against a key/value cache on the GPU against the fp64 oracle:
+grouped heads, several new tokens, empty and short caches, one chunk and
+many chunks, and the full-size decode batch."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_113_amd as fa
+import oracle.attention as orc
+import workloads
+from gpu_util import assert_close, assert_lse_close, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def cache_inputs(B, cap, s_q, H, H_kv, D, dtype, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    td = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    q = torch.randn((B, s_q, H, D), generator=g).to(td)
+    k = torch.randn((B, cap, H_kv, D), generator=g).to(td)
+    v = torch.randn((B, cap, H_kv, D), generator=g).to(td)
+    return q.to(DEV), k.to(DEV), v.to(DEV)
+
+
+def check(name, o, lse, q, k, v, lens, scale, dtype, strict=False):
+    ro, rl = orc.attention_decode(to64(q), to64(k), to64(v), lens, scale)
+    go, gl = to64(o), to64(lse)
+    empty = np.isneginf(rl)                       # [B, H, s_q]: rows that see no key
+    assert np.array_equal(np.isneginf(gl), empty), name + ": -inf LSE rows differ"
+    assert (go.transpose(0, 2, 1, 3)[empty] == 0).all(), name + ": rows without keys not 0"
+    seen = ~empty.transpose(0, 2, 1)              # [B, s_q, H]
+    if seen.any():
+        assert_close(name + " O", go[seen], ro[seen], dtype, strict=strict)
+        assert_lse_close(name, gl[~empty], rl[~empty])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H_kv,s_q", [(8, 1), (2, 1), (1, 1), (2, 4), (1, 4)])
+def test_decode_chunked(dtype, D, H_kv, s_q):
+    """Caches of length 0, 1, 3, 333 and 700 (capacity 700), cut into
+    128-key chunks merged by LSE; with s_q = 4 some rows see no key."""
+    lens = [0, 1, 3, 333, 700]
+    q, k, v = cache_inputs(5, 700, s_q, 8, H_kv, D, dtype, seed=500 + D + 10 * H_kv + s_q)
+    assert fa.decode_workspace_bytes(5, s_q, 8, H_kv, 700, D) > 0
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = fa.decode(q, k, v, lt, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    check(f"{dtype} D{D} H8/{H_kv} s_q={s_q}", o, lse, q, k, v, lens, D ** -0.5, dtype)
+
+
+def test_decode_single_chunk():
+    """Many (sequence, K/V head) pairs and short caches: one chunk per
+    workgroup, results written directly."""
+    B, cap = 64, 300
+    g = torch.Generator(device="cpu")
+    g.manual_seed(71)
+    lens = [int(x) for x in torch.randint(1, cap + 1, (B,), generator=g)]
+    assert fa.decode_workspace_bytes(B, 1, 32, 32, cap, 128) == 0
+    q, k, v = cache_inputs(B, cap, 1, 32, 32, 128, "bf16", seed=72)
+    o, lse = fa.decode(q, k, v, torch.tensor(lens, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    check("single chunk", o, lse, q, k, v, lens, 128 ** -0.5, "bf16", strict=True)
+
+
+def test_decode_lengths_clamped():
+    """Lengths above max_seqlen_k are read as max_seqlen_k; a negative length
+    as 0."""
+    q, k, v = cache_inputs(3, 512, 1, 8, 2, 128, "bf16", seed=81)
+    lt = torch.tensor([300, -5, 512], dtype=torch.int32, device=DEV)
+    o, lse = fa.decode(q, k, v, lt, max_seqlen_k=200)
+    torch.cuda.synchronize()
+    check("clamped", o, lse, q, k, v, [200, 0, 200], 128 ** -0.5, "bf16")
+
+
+def test_decode_negative_and_zero_scale():
+    q, k, v = cache_inputs(2, 257, 2, 8, 4, 64, "bf16", seed=91)
+    lens = [257, 130]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    for scale in (-0.2, 0.0):
+        o, lse = fa.decode(q, k, v, lt, scale=scale)
+        torch.cuda.synchronize()
+        check(f"scale {scale}", o, lse, q, k, v, lens, scale, "bf16")
+
+
+def test_decode_batch_workload():
+    """The benchmark's decode step (16 sequences, caches of 1k..16k tokens,
+    32 query over 8 K/V heads, D = 128) on every row at full size."""
+    w = workloads.decode_gqa()
+    q, k, v, lt = workloads.make_decode_inputs(w, device=DEV)
+    o, lse = fa.decode(q, k, v, lt, scale=w.scale)
+    torch.cuda.synchronize()
+    check("decode batch", o, lse, q, k, v, list(w.lengths), w.scale, "bf16", strict=True)
+
+
+def test_decode_repeatable_and_workspace_reuse():
+    """Same inputs twice through one caller-owned workspace: identical bits."""
+    q, k, v = cache_inputs(4, 2048, 1, 16, 2, 128, "bf16", seed=95)
+    lt = torch.tensor([2048, 1000, 17, 1500], dtype=torch.int32, device=DEV)
+    ws = torch.empty(fa.decode_workspace_bytes(4, 1, 16, 2, 2048, 128), dtype=torch.uint8,
+                     device=DEV)
+    o1, l1 = fa.decode(q, k, v, lt, workspace=ws)
+    o2, l2 = fa.decode(q, k, v, lt, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -164,6 +164,71 @@ def make_varlen_inputs(w: VarlenWorkload, device="cpu"):
     return q.to(device), k.to(device), v.to(device), cu.to(device)
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """s_q new tokens per sequence against a K/V cache of capacity cap."""
+    name: str
+    lengths: tuple
+    cap: int
+    s_q: int
+    H: int
+    H_kv: int
+    D: int
+    dtype: str
+    seed: int
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    @property
+    def B(self):
+        return len(self.lengths)
+
+    def bytes_moved(self):
+        """K and V of every cached token read once, Q read, O and LSE written."""
+        esize = torch.empty((), dtype=self.torch_dtype).element_size()
+        kv = 2 * sum(self.lengths) * self.H_kv * self.D * esize
+        qo = 2 * self.B * self.s_q * self.H * self.D * esize
+        return kv + qo + 4 * self.B * self.H * self.s_q
+
+    def flops(self):
+        """4 D per (query row, visible key) pair."""
+        f = 0
+        for L in self.lengths:
+            for t in range(self.s_q):
+                f += 4 * self.H * self.D * max(0, min(L, L - self.s_q + t + 1))
+        return float(f)
+
+
+def decode_gqa():
+    """Decode step of 16 sequences with cached lengths uniform in
+    [1024, 16384] (seeded), one new token each, 32 query heads over 8 K/V
+    heads, D = 128, bf16, cache capacity 16384."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(5)
+    lengths = tuple(int(x) for x in torch.randint(1024, 16385, (16,), generator=g))
+    return DecodeWorkload("bf16 decode 16 seqs cache 1k..16k H32/8 D128 s_q=1", lengths, 16384,
+                          1, 32, 8, 128, "bf16", 5)
+
+
+def make_decode_inputs(w: DecodeWorkload, device="cpu"):
+    """q [B, s_q, H, D], k_cache, v_cache [B, cap, H_kv, D] from one generator
+    seeded with w.seed (drawn in the order q, k, v; slots past a sequence's
+    length hold draws too), and cache_seqlens int32 [B]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    q = torch.randn((w.B, w.s_q, w.H, w.D), generator=g).to(w.torch_dtype)
+    k = torch.randn((w.B, w.cap, w.H_kv, w.D), generator=g).to(w.torch_dtype)
+    v = torch.randn((w.B, w.cap, w.H_kv, w.D), generator=g).to(w.torch_dtype)
+    lens = torch.tensor(w.lengths, dtype=torch.int32)
+    return q.to(device), k.to(device), v.to(device), lens.to(device)
+
+
 def all_workloads():
     return [fp32_small(), bf16_short(), fp16_causal_4k()] + bf16_causal_sweep() + [
         bf16_training()]
