@@ -12,17 +12,24 @@
 // tokens become the rows of one 32-row MFMA tile, so every K/V byte is read
 // once per step. Its four waves take every fourth 32-key block of the chunk
 // and keep their own online-softmax state (running maximum, running sum,
-// fp32 accumulator: "From Self-Attention to FlashAttention", section 2); each
-// wave streams its blocks through its own double-buffered LDS region with
-// direct global->LDS loads, so the key loop needs no workgroup barrier. At
+// fp32 accumulator: "From Self-Attention to FlashAttention", section 2). Each
+// wave loads its blocks itself, one block ahead: K straight into registers
+// (the score MFMA's A operand) and V through its own double-buffered LDS
+// region (direct global->LDS loads; the P V product reads it transposed),
+// so the key loop needs no workgroup barrier, and two workgroups fit on a
+// CU to keep enough bytes in flight for HBM. At
 // the end the four partial states are merged through LDS with the same
 // rescale-and-add, and the chunk's (O, LSE) is written: straight to the
 // output when the cache is one chunk, else to a workspace that
 // decode_merge_kernel combines over the chunks by LSE.
 //
-// Products and layouts follow the forward kernel: S^T = K Q^T and
-// O^T = V^T P^T on 32x32x16 MFMAs, K rows with an XOR chunk swizzle, V read
-// transposed from LDS with ds_read_b64_tr_b16.
+// Products follow the forward kernel: S^T = K Q^T and O^T = V^T P^T on
+// 32x32x16 MFMAs, V read transposed from LDS with ds_read_b64_tr_b16. The
+// head dim is split between the two lane halves of the score MFMA as
+// d = (D/2) * half + 8 * step + element, the same for K and Q, so that each
+// lane reads one contiguous half row of K.
+#include <utility>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -36,6 +43,53 @@ constexpr int kDKB = 32;  // keys per block
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Loads whose completion the kernel tracks itself. The compiler's own
+// counting of outstanding loads turns conservative (a wait for all of them)
+// once direct global->LDS loads are in flight, which would serialise the
+// one-block-ahead prefetch; these are issued as plain instructions instead,
+// and every value they produce passes through an explicit s_waitcnt that
+// names it as an operand before its first use.
+template <int I>
+__device__ __forceinline__ void load16_async(u32x4& dst, const uint16_t* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst) : "v"(p), "n"(16 * I));
+}
+template <int KK, int... I>
+__device__ __forceinline__ void load_row_async(u32x4 (&dst)[KK], const uint16_t* p,
+                                               std::integer_sequence<int, I...>) {
+  (load16_async<I>(dst[I], p), ...);
+}
+// Wait until at most N vector-memory loads are outstanding; `k` are the
+// registers the waited loads wrote.
+template <int N>
+__device__ __forceinline__ void wait_vm(u32x4 (&k)[8]) {
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]), "+v"(k[4]), "+v"(k[5]),
+                 "+v"(k[6]), "+v"(k[7])
+               : "n"(N)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm(u32x4 (&k)[4]) {
+  asm volatile("s_waitcnt vmcnt(%4)"
+               : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3])
+               : "n"(N)
+               : "memory");
+}
+// The LDS reads are complete (s_waitcnt lgkmcnt(0) just before); this ties
+// their registers to that point so no use moves above it.
+__device__ __forceinline__ void wait_lgkm_tied(u32x4 (&a)[8]) {
+  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+               "+v"(a[6]), "+v"(a[7]));
+}
+__device__ __forceinline__ void wait_lgkm_tied(u32x4 (&a)[4]) {
+  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+}
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
 
 struct DecParams {
   const uint16_t* q;        // [B, s_q, H, D]
@@ -52,7 +106,7 @@ struct DecParams {
 };
 
 template <typename TT, int D>
-__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams prm) {
+__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecParams prm) {
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int ROWB = 2 * D;              // bytes per row
   constexpr int BLKB = kDKB * ROWB;        // bytes of one K or V block
@@ -61,10 +115,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams 
   constexpr int DB = D / 32;               // 32-row blocks of the head dim
   constexpr int KK = D / 16;               // k-steps of the score MFMA
   constexpr int OC = D / 4;                // 16-byte chunks of an fp32 output row
-  static_assert(kDecWaves * 2 * BLKB >= kDecWaves * 32 * D * 4, "merge buffer too small");
-  // Per wave: K block then V block, one region per buffer.
-  __shared__ __attribute__((aligned(1024))) char buf0[kDecWaves * 2 * BLKB];
-  __shared__ __attribute__((aligned(1024))) char buf1[kDecWaves * 2 * BLKB];
+  constexpr int SLAB = 32 * D * 4;         // one wave's fp32 rows in the merge
+  static_assert(kDecWaves * BLKB >= 2 * SLAB, "merge buffer too small");
+  // Per wave: one V block per buffer. The merge reuses both buffers, two
+  // waves' slabs in each.
+  __shared__ __attribute__((aligned(1024))) char vb0[kDecWaves * BLKB];
+  __shared__ __attribute__((aligned(1024))) char vb1[kDecWaves * BLKB];
   __shared__ float stat_m[kDecWaves][32];
   __shared__ float stat_l[kDecWaves][32];
 
@@ -96,10 +152,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams 
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *(const u32x4*)(qrow + 16 * kk + 8 * hi);
+      if (row_ok) x = *(const u32x4*)(qrow + (D / 2) * hi + 8 * kk);
       qf[kk] = x ^ prm.qsign;
     }
   }
+  wait_vm<0>(qf);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -116,38 +173,40 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams 
   auto vswz = [](int r) __attribute__((always_inline)) {
     return CH == 16 ? 4 * (r & 3) : 2 * (r & 3);
   };
-  // Direct loads of block j's 32 K rows and 32 V rows into this wave's
-  // region; rows past the cache length repeat its last row (masked).
-  auto load_block = [&](int j, char* kdst, char* vdst) __attribute__((always_inline)) {
+  // Block j's loads: K row lq's half `hi` into registers (the score MFMA's
+  // A operand), the 32 V rows into this wave's LDS region by direct loads.
+  // Rows past the cache length repeat its last row (their scores are
+  // masked). With live = false every lane reads the last row: a load that
+  // keeps the loop free of branches (and so keeps the compiler's memory
+  // counters exact) but whose data is never used.
+  auto load_block = [&](int j, bool live, u32x4 (&kr)[KK], char* vdst)
+      __attribute__((always_inline)) {
     const int key0 = k_lo + kDKB * j;
+    const uint16_t* krow =
+        Kb + (size_t)(live ? min(key0 + lq, L - 1) : L - 1) * kv_stride + (D / 2) * hi;
+    load_row_async<KK>(kr, krow, std::make_integer_sequence<int, KK>{});
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
       const int R0 = i * RPI;
       const int r = R0 + lane / CH, p = lane % CH;
-      const size_t grow = (size_t)min(key0 + r, L - 1) * kv_stride;
-      const void* ksrc = Kb + grow + (p ^ (r % CH)) * 8;
-      const void* vsrc = Vb + grow + (p ^ vswz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + R0 * ROWB), 16, 0, 0);
+      const int row = live ? min(key0 + r, L - 1) : L - 1;
+      const void* vsrc = Vb + (size_t)row * kv_stride + (p ^ vswz(r)) * 8;
       __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + R0 * ROWB), 16, 0, 0);
     }
   };
 
-  const int kxor = lq % CH;
-  const int koff = lq * ROWB;
   const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1;
   const int vlane = (4 * hi + tj) * ROWB + 8 * (tm & 1);
   const int vx = (2 * dsub + (tm >> 1)) ^ vswz(tj);
 
   // One 32-key block: scores, masked online softmax, P V.
-  auto compute_block = [&](int j, const char* kt, const char* vt) __attribute__((always_inline)) {
+  auto compute_block = [&](int j, const u32x4 (&kr)[KK], const char* vt)
+      __attribute__((always_inline)) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 a = *(const u32x4*)(kt + koff + 16 * ((2 * kk + hi) ^ kxor));
-      s = TT::mma(a, qf[kk], s);
-    }
+    for (int kk = 0; kk < KK; ++kk) s = TT::mma(kr[kk], qf[kk], s);
     const int key0 = k_lo + kDKB * j;
     uint32_t okm = 0;
     float mx = -INFINITY;
@@ -185,47 +244,47 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams 
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pf[hh][e] = TT::pack2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+    // V's transposed reads (the direct loads that filled this buffer are
+    // complete: the loop waited for them).
+    u32x4 va[2 * DB];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* base = vt + vlane + 16 * hh * ROWB + 16 * ((4 * db) ^ vx);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 u2 = __builtin_bit_cast(u32x2, up);
-        const u32x4 a = {l2[0], l2[1], u2[0], u2[1]};
-        oacc[db] = TT::mma(a, pf[hh], oacc[db]);
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)(vt + vlane + 16 * hh * ROWB +
+                                                               16 * ((4 * db) ^ vx));
+        const u32x2 lo = lds_read_tr16(base);
+        const u32x2 up = lds_read_tr16(base + 8 * ROWB);
+        va[hh * DB + db] = u32x4{lo[0], lo[1], up[0], up[1]};
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_lgkm_tied(va);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = TT::mma(va[hh * DB + db], pf[hh], oacc[db]);
   };
 
-  // This wave's blocks w, w + 4, ...: block i of the wave in buffer i % 2,
-  // the next one loading while the current one is computed. A wave reads
-  // only what it loaded itself, so its own vmcnt wait is the only sync.
-  char* k0 = buf0 + w * 2 * BLKB;
-  char* v0 = k0 + BLKB;
-  char* k1 = buf1 + w * 2 * BLKB;
-  char* v1 = k1 + BLKB;
+  // This wave's blocks w, w + 4, ...: block i of the wave in register set
+  // and V buffer i % 2, the next one loading while the current one is
+  // computed (past the last block, a dummy load takes its place). A wave
+  // reads only what it loaded itself, so waiting until at most the next
+  // block's KK + LPB loads are in flight is the only sync; the LDS reads of
+  // a buffer are complete before the next direct load into it is issued.
+  u32x4 kA[KK], kB[KK];
+  char* v0 = vb0 + w * BLKB;
+  char* v1 = vb1 + w * BLKB;
   const int ni = nblk > w ? (nblk - w + kDecWaves - 1) / kDecWaves : 0;
-  if (ni > 0) load_block(w, k0, v0);
+  if (ni > 0) load_block(w, true, kA, v0);
   for (int i = 0; i < ni; i += 2) {
-    if (i + 1 < ni) {
-      load_block(w + kDecWaves * (i + 1), k1, v1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPB) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    compute_block(w + kDecWaves * i, k0, v0);
-    if (i + 1 < ni) {
-      if (i + 2 < ni) {
-        load_block(w + kDecWaves * (i + 2), k0, v0);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPB) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      compute_block(w + kDecWaves * (i + 1), k1, v1);
-    }
+    load_block(w + kDecWaves * (i + 1), i + 1 < ni, kB, v1);
+    wait_vm<KK + LPB>(kA);  // block i (K in kA, V in v0) has landed
+    compute_block(w + kDecWaves * i, kA, v0);
+    load_block(w + kDecWaves * (i + 2), i + 2 < ni, kA, v0);
+    wait_vm<KK + LPB>(kB);
+    if (i + 1 < ni) compute_block(w + kDecWaves * (i + 1), kB, v1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Merge the four waves' states: maximum M over the waves, each wave's
   // weight 2^(m_w - M) (0 for a wave that saw no key), total sum, and the
@@ -252,7 +311,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams 
     const float f = mrun == -INFINITY ? 0.f : fast_exp2(mrun - M);
     // Row lq of wave w's slab, 16-byte chunk c stored at c ^ (lq % OC) so
     // that the 32 rows written together spread over the banks.
-    float* ob = (float*)buf0 + (size_t)(w * 32 + lq) * D;
+    float* ob = (float*)((w < 2 ? vb0 : vb1) + (w & 1) * SLAB) + (size_t)lq * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -277,7 +336,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(const DecParams 
       for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int x = 0; x < kDecWaves; ++x) {
-        const float* src = (const float*)buf0 + (size_t)(x * 32 + row) * D;
+        const float* src = (const float*)((x < 2 ? vb0 : vb1) + (x & 1) * SLAB) + (size_t)row * D;
 #pragma unroll
         for (int e = 0; e < SEG; e += 4) {
           const f32x4 y = *(const f32x4*)(src + 4 * (((d0 + e) / 4) ^ (row % OC)));
@@ -320,10 +379,18 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
 // Combine the chunks of one output row (b, h, t), one wave per row:
 // LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s; chunks with
 // LSE_s = -inf carry no weight, and a row with none left is O = 0,
-// LSE = -inf.
+// LSE = -inf. Lane s holds chunk s's LSE and weight (at most 64 chunks);
+// the partial outputs are loaded eight chunks at a time before any is
+// used, so the loads overlap.
 template <typename TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
@@ -331,36 +398,43 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
                                                            float* __restrict__ lse, int n_rows,
                                                            int n_splits, int heads, int s_q) {
   constexpr int PER = D / 64;
+  constexpr int U = 8;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;
-  const float* pl = part_lse + (size_t)row * n_splits;
-  float m = -INFINITY;
-  for (int s = lane; s < n_splits; s += 64) m = fmaxf(m, pl[s]);
-  m = wave_max(m);
+  const float ls = lane < n_splits ? part_lse[(size_t)row * n_splits + lane] : -INFINITY;
+  const float m = wave_max(ls);
+  const float wt = (ls == -INFINITY) ? 0.f : __expf(ls - m);
+  const float wsum = wave_sum(wt);
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float ls = pl[s];
-      const float wt = ls == -INFINITY ? 0.f : __expf(ls - m);
-      wsum += wt;
-      const float* src = part_o + ((size_t)row * n_splits + s) * D + lane * PER;
+  const float* src = part_o + (size_t)row * n_splits * D + lane * PER;
+  for (int s0 = 0; s0 < n_splits; s0 += U) {
+    float val[U][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, src[e], acc[e]);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        val[u][e] = s0 + u < n_splits ? src[(size_t)(s0 + u) * D + e] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float ws = s0 + u < n_splits
+                           ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                           __builtin_bit_cast(int, wt), s0 + u))
+                           : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = ws != 0.f ? fmaf(ws, val[u][e], acc[e]) : acc[e];
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int t = row % s_q, bh = row / s_q;
   const int b = bh / heads, h = bh - b * heads;
   uint16_t* dst = o + ((size_t)(b * s_q + t) * heads + h) * D + lane * PER;
-  if (PER == 2) {
-    *(uint32_t*)dst = TT::pack2(acc[0] * inv, acc[PER - 1] * inv);
+  if constexpr (PER == 2) {
+    *(uint32_t*)dst = TT::pack2(acc[0] * inv, acc[1] * inv);
   } else {
-    const uint32_t x = TT::pack2(acc[0] * inv, 0.f);
-    *dst = (uint16_t)(x & 0xffffu);
+    *dst = (uint16_t)(TT::pack2(acc[0] * inv, 0.f) & 0xffffu);
   }
   if (lane == 0) lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }

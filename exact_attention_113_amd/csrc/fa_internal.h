@@ -70,7 +70,10 @@ struct DecodeArgs {
 
 // How the cache is cut into chunks (one workgroup per sequence, K/V head and
 // chunk) and where the per-chunk partial results go in the workspace.
-constexpr int64_t kDecodeTargetWgs = 2048;
+#ifndef FA_DECODE_TARGET_WGS
+#define FA_DECODE_TARGET_WGS 4096
+#endif
+constexpr int64_t kDecodeTargetWgs = FA_DECODE_TARGET_WGS;
 constexpr int64_t kMaxSplits = 64;
 struct DecodePlan {
   int n_splits, chunk;
