@@ -389,7 +389,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s; chunks with
 // LSE_s = -inf carry no weight, and a row with none left is O = 0,
 // LSE = -inf. Lane s holds chunk s's LSE and weight (at most 64 chunks);
-// the partial outputs are loaded eight chunks at a time before any is
+// the partial outputs are loaded 32 chunks at a time before any is
 // used, so the loads overlap.
 template <typename TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
                                                            float* __restrict__ lse, int n_rows,
                                                            int n_splits, int heads, int s_q) {
   constexpr int PER = D / 64;
-  constexpr int U = 8;
+  constexpr int U = 32;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;

@@ -1,6 +1,6 @@
 // Fused attention forward for bf16/fp16 inputs on gfx950.
 //
-// One workgroup owns BM = 256 query rows of one (batch, head) and streams
+// One workgroup owns BM = 256 (or 128) query rows of one (batch, head) and streams
 // the key/value rows through LDS, keeping per query row a running maximum,
 // a running sum of exponentials and an unnormalised fp32 output accumulator
 // (online softmax: "From Self-Attention to FlashAttention", section 2;
@@ -9,7 +9,8 @@
 // logsumexp are the only results written back (the flash data flow of
 // section 1 of the first page: only O goes back to HBM).
 //
-// Waves. Eight waves, two per SIMD, each owning 32 consecutive query rows.
+// Waves. Eight waves, two per SIMD (four for short sequences, two
+// workgroups per CU), each owning 32 consecutive query rows.
 // Scores are computed transposed, S^T = K Q^T (32x32x16 MFMA, fp32
 // accumulate): lane j and j + 32 share one query and each holds 16 of a
 // 32-key block's scores, so row maxima and sums are in-register reductions
@@ -45,9 +46,16 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 8;               // two per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;        // query rows per workgroup (32 per wave)
+// Waves per workgroup (NW, 32 query rows each): 8 (two per SIMD, one
+// workgroup per CU) when that gives at least kMinGrid workgroups, else 4
+// (128 rows, two workgroups per CU) so that short sequences spread over
+// more CUs. Each wave runs the same code in both cases, so the results are
+// identical. (Two waves of 64 rows measured slower than four: with 64 KiB
+// of LDS per workgroup they leave one wave per SIMD.)
+#ifndef FA_FWD_MIN_GRID
+#define FA_FWD_MIN_GRID 512
+#endif
+constexpr int64_t kMinGrid = FA_FWD_MIN_GRID;  // workgroups wanted before shrinking them
 constexpr int kBN = 64;                 // keys per LDS tile
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
@@ -104,14 +112,14 @@ struct FwdParams {
   uint32_t qsign;
 };
 
-template <typename TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
-    const FwdParams prm) {
+template <typename TT, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const FwdParams prm) {
+  constexpr int kBM = 32 * NW;                // query rows per workgroup
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                 // bytes per row
   constexpr int TILEB = kBN * ROWB;           // bytes per K or V tile
   constexpr int RPI = 64 / CH;                // rows per wave-wide direct load (1 KiB)
-  constexpr int LPW = kBN / (kWaves * RPI);   // direct loads per wave, tile and tensor
+  constexpr int LPW = kBN / (NW * RPI);       // direct loads per wave, tile and tensor
   constexpr int DB = D / 32;                  // 32-row blocks of the head dim
   constexpr int KK = D / 16;                  // k-steps of the score MFMA
   static_assert(LPW >= 1, "tile too small for one direct load per wave");
@@ -478,17 +486,23 @@ hipError_t launch_half(const FwdArgs& a) {
   p.total = (int)a.total;
   p.heads = (int)a.H;
   p.group = (int)(a.H / a.H_kv);
-  p.n_qtiles = (int)((a.N + kBM - 1) / kBM);
   p.bh_count = (int)(a.B * a.H);
   p.c = fabsf(a.scale) * kLog2e;
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  const int64_t grid = (int64_t)p.n_qtiles * p.bh_count;
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<TT, D, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       a.stream, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<TT, D, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       a.stream, p);
+  auto go = [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    p.n_qtiles = (int)((a.N + 32 * NW - 1) / (32 * NW));
+    const int64_t grid = (int64_t)p.n_qtiles * p.bh_count;
+    if (a.causal)
+      hipLaunchKernelGGL((fwd_kernel<TT, D, true, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                         a.stream, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<TT, D, false, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                         a.stream, p);
+  };
+  const int64_t bh = a.B * a.H;
+  if (((a.N + 255) / 256) * bh >= kMinGrid) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }
 
