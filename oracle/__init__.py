@@ -15,11 +15,14 @@ Sources (pages cited by title and section):
        "A surprise" (the backward remark).
 """
 
+from . import rng  # noqa: F401
 from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_online,
     attention_forward_varlen,
     attention_decode,
+    attention_forward_dropout,
+    attention_backward_dropout,
     merge_partials,
     attention_backward,
     attention_probabilities,

@@ -40,6 +40,8 @@ blockwise algorithm for the "online equals three-pass" invariant.
 
 import numpy as np
 
+from oracle import rng as _rng
+
 # Query rows handled per chunk: bounds the materialised S/P to
 # ROW_CHUNK x N fp64 values per (batch, head) without changing any result
 # (each query row is computed on its own).
@@ -300,3 +302,74 @@ def merge_partials(o_parts, lse_parts):
                  (w[..., None] * o_parts).sum(axis=0) / np.where(total > 0, total, 1.0)[..., None],
                  0.0)
     return o, lse
+
+
+def attention_forward_dropout(q, k, v, scale, causal, p, seed, offset):
+    """Exact attention with dropout on the probabilities (fp64).
+
+    The dropout branch that the verification answer of "Flash Attention
+    algorithm design and I/O optimisation" asks to cover, read as the usual
+    attention dropout: P is the softmax of the scores as in
+    attention_forward (so LSE is unchanged), each probability is kept or
+    dropped by the counter-based bits of oracle.rng.keep_mask, and
+        O = (P * keep) V / (1 - p_eff),   p_eff = dropout_threshold(p) / 256.
+
+    q, k, v: [B, H, N, D]. Returns (O, LSE).
+    """
+    q, k, v = _check(q, k, v)
+    B, H, N, D = q.shape
+    inv_keep = 1.0 / (1.0 - _rng.dropout_threshold(p) / 256.0)
+    o = np.empty((B, H, N, D))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, ROW_CHUNK):
+                r1 = min(N, r0 + ROW_CHUNK)
+                s = _scores(q[b, h, r0:r1], k[b, h], scale, r0, causal)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                prob = e / l
+                keep = _rng.keep_mask(b * H + h, np.arange(r0, r1), np.arange(N), p, seed, offset)
+                o[b, h, r0:r1] = (np.where(keep, prob, 0.0) @ v[b, h]) * inv_keep
+                lse[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
+    """dQ, dK, dV of attention_forward_dropout for upstream gradient dO (fp64).
+
+    With the keep decisions fixed, the forward is a smooth function of
+    Q, K, V; its exact gradient is the chain rule through the scaled mask
+    and the softmax:
+        Pd = P * keep / (1 - p_eff),  dV = Pd^T dO,
+        dP = (dO V^T) * keep / (1 - p_eff),  delta = rowsum(P * dP),
+        dS = P * (dP - delta),  dQ = scale * dS K,  dK = scale * dS^T Q.
+    """
+    q, k, v = _check(q, k, v)
+    do = np.asarray(do, dtype=np.float64)
+    if do.shape != q.shape:
+        raise ValueError("do must have q's shape")
+    B, H, N, D = q.shape
+    inv_keep = 1.0 / (1.0 - _rng.dropout_threshold(p) / 256.0)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(q)
+    dv = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, ROW_CHUNK):
+                r1 = min(N, r0 + ROW_CHUNK)
+                s = _scores(q[b, h, r0:r1], k[b, h], scale, r0, causal)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                prob = e / e.sum(axis=1, keepdims=True)
+                keep = _rng.keep_mask(b * H + h, np.arange(r0, r1), np.arange(N), p, seed, offset)
+                scale_keep = np.where(keep, inv_keep, 0.0)
+                g = do[b, h, r0:r1]
+                dv[b, h] += (prob * scale_keep).T @ g
+                dp = (g @ v[b, h].T) * scale_keep
+                delta = (prob * dp).sum(axis=1, keepdims=True)
+                ds = prob * (dp - delta)
+                dq[b, h, r0:r1] = scale * (ds @ k[b, h])
+                dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])
+    return dq, dk, dv

@@ -465,6 +465,143 @@ def pin_merge_partials(orc):
 
 DECODE_PINS = [pin_decode_brute_force, pin_decode_is_causal_suffix, pin_merge_partials]
 
+# --- dropout ------------------------------------------------------------------
+
+# Known-answer vectors of Philox4x32-10 (counter, key) -> output, as published
+# with the generator's reference implementation (Random123).
+PHILOX_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
+     (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+def _philox_scalar(ctr, key):
+    """Philox4x32-10 on Python integers, one counter at a time."""
+    c0, c1, c2, c3 = ctr
+    k0, k1 = key
+    for _ in range(10):
+        p0 = 0xD2511F53 * c0
+        p1 = 0xCD9E8D57 * c2
+        c0, c1, c2, c3 = ((p1 >> 32) ^ c1 ^ k0, p1 & 0xFFFFFFFF, (p0 >> 32) ^ c3 ^ k1,
+                          p0 & 0xFFFFFFFF)
+        k0 = (k0 + 0x9E3779B9) & 0xFFFFFFFF
+        k1 = (k1 + 0xBB67AE85) & 0xFFFFFFFF
+    return c0, c1, c2, c3
+
+
+def pin_philox_known_answers(orc):
+    """The oracle's vectorised generator reproduces the published vectors."""
+    for ctr, key, out in PHILOX_KAT:
+        assert _philox_scalar(ctr, key) == out
+        got = orc._rng.philox4x32_10(*ctr, *key)
+        assert tuple(int(x) for x in got) == out
+
+
+def brute_force_dropout(q, k, v, scale, causal, p, seed, offset):
+    """Scalar loops: keep bit of (b, h, i, j) from one Philox call per 4x4
+    block (word i % 4, byte j % 4 of counter (j//4, i//4, b*H + h, offset)),
+    dropped when the byte is below floor(256 p + 0.5)."""
+    B, H, N, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    thr = math.floor(float(np.float32(p)) * 256.0 + 0.5)
+    inv_keep = 1.0 / (1.0 - thr / 256.0)
+    key = (seed & 0xFFFFFFFF, seed >> 32)
+    o = [[[[0.0] * D for _ in range(N)] for _ in range(H)] for _ in range(B)]
+    lse = [[[0.0] * N for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = range(i + 1) if causal else range(N)
+                sc = [scale * sum(q[b][h][i][t] * k[b][h][j][t] for t in range(D)) for j in keys]
+                m = max(sc)
+                wts = [math.exp(x - m) for x in sc]
+                tot = sum(wts)
+                lse[b][h][i] = m + math.log(tot)
+                for j, wt in zip(keys, wts):
+                    word = _philox_scalar((j // 4, i // 4, b * H + h, offset), key)[i % 4]
+                    if (word >> (8 * (j % 4))) & 0xFF < thr:
+                        continue
+                    for t in range(D):
+                        o[b][h][i][t] += wt / tot * inv_keep * v[b][h][j][t]
+    return o, lse
+
+
+def pin_dropout_brute_force(orc):
+    """Dropout forward against scalar loops with their own generator (two
+    heads, N = 9 crossing 4x4 block edges, a 64-bit seed and an offset)."""
+    q, k, v = (_rand((1, 2, 9, 3), s) for s in (81, 82, 83))
+    seed = 0x1234_5678_9ABC_DEF0
+    for causal in (False, True):
+        for pr in (0.3, 0.5):
+            o, lse = orc.attention_forward_dropout(q, k, v, 0.7, causal, pr, seed, 5)
+            bo, bl = brute_force_dropout(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, pr,
+                                         seed, 5)
+            np.testing.assert_allclose(o, np.array(bo), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-12)
+
+
+def pin_dropout_p_zero(orc):
+    """p = 0 keeps everything: forward and backward equal the plain ones."""
+    q, k, v, g = (_rand((2, 2, 11, 4), s) for s in (84, 85, 86, 87))
+    for causal in (False, True):
+        o, lse = orc.attention_forward_dropout(q, k, v, 0.6, causal, 0.0, 99, 0)
+        ro, rl = orc.attention_forward(q, k, v, 0.6, causal)
+        np.testing.assert_allclose(o, ro, rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(lse, rl)
+        grads = orc.attention_backward_dropout(q, k, v, g, 0.6, causal, 0.0, 99, 0)
+        refs = orc.attention_backward(q, k, v, g, 0.6, causal)
+        for a, r in zip(grads, refs):
+            np.testing.assert_allclose(a, r, rtol=0, atol=1e-13)
+
+
+def pin_dropout_keep_rate(orc):
+    """The fraction kept over 2 heads x 512 x 512 elements is within five
+    standard deviations of 1 - floor(256 p + 0.5) / 256, and masks of
+    different heads, offsets or seeds differ as independent ones would."""
+    n = 512
+    for pr in (0.1, 0.5):
+        thr = math.floor(pr * 256 + 0.5)
+        keep_p = 1 - thr / 256
+        masks = [orc._rng.keep_mask(bh, np.arange(n), np.arange(n), pr, seed, off)
+                 for bh, seed, off in ((0, 7, 0), (1, 7, 0), (0, 7, 1), (0, 8, 0))]
+        total = np.concatenate([m.ravel() for m in masks[:2]])
+        sd = math.sqrt(keep_p * (1 - keep_p) / total.size)
+        assert abs(total.mean() - keep_p) < 5 * sd, (total.mean(), keep_p)
+        differ = 2 * keep_p * (1 - keep_p)
+        for other in masks[1:]:
+            frac = (other != masks[0]).mean()
+            assert abs(frac - differ) < 5 * math.sqrt(differ * (1 - differ) / other.size)
+
+
+def pin_dropout_finite_differences(orc):
+    """With the keep bits fixed the dropout forward is smooth in Q, K, V; its
+    central differences match the dropout backward."""
+    q, k, v, g = (_rand((1, 1, 6, 3), s) for s in (91, 92, 93, 94))
+    for causal in (False, True):
+        grads = orc.attention_backward_dropout(q, k, v, g, 0.8, causal, 0.4, 2024, 3)
+        for idx, x in enumerate((q, k, v)):
+            num = np.zeros_like(x)
+            for pos in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[pos] += 1e-6
+                xm[pos] -= 1e-6
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[idx], args_m[idx] = xp, xm
+                fp = (orc.attention_forward_dropout(*args_p, 0.8, causal, 0.4, 2024, 3)[0] * g).sum()
+                fm = (orc.attention_forward_dropout(*args_m, 0.8, causal, 0.4, 2024, 3)[0] * g).sum()
+                num[pos] = (fp - fm) / 2e-6
+            err = np.abs(num - grads[idx]).max() / max(1.0, np.abs(num).max())
+            assert err < 1e-7, (idx, causal, err)
+
+
+DROPOUT_PINS = [pin_philox_known_answers, pin_dropout_brute_force, pin_dropout_p_zero,
+                pin_dropout_keep_rate, pin_dropout_finite_differences]
+
+
 
 FORWARD_PINS = [pin_golden_forward, pin_brute_force, pin_online_equals_three_pass,
                 pin_rows_sum_to_one, pin_constant_v, pin_causal_row0, pin_scale_zero,
@@ -472,4 +609,4 @@ FORWARD_PINS = [pin_golden_forward, pin_brute_force, pin_online_equals_three_pas
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_grad_sums,
                  pin_constant_v_grads, pin_scale_zero_grads, pin_delta_two_ways,
                  pin_torch_autograd]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS + DECODE_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS + DECODE_PINS + DROPOUT_PINS

@@ -9,8 +9,9 @@ import pytest
 
 from oracle_pins import ALL_PINS
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "oracle", "attention.py")
+ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE, "attention.py")
+RNG_SRC = os.path.join(ORACLE, "rng.py")
 
 MUTANTS = {
     "mask_excludes_diagonal": ("s = np.where(kj > qi, -np.inf, s)\n    return s",
@@ -58,24 +59,58 @@ MUTANTS = {
                             "                hk = h % H_kv\n                s = scale"),
     "merge_unweighted": ("(w[..., None] * o_parts).sum(axis=0)", "o_parts.sum(axis=0)"),
     "merge_lse_drops_max": ("safe_m + np.log(", "np.log("),
+    "dropout_no_rescale": ("o[b, h, r0:r1] = (np.where(keep, prob, 0.0) @ v[b, h]) * inv_keep",
+                           "o[b, h, r0:r1] = (np.where(keep, prob, 0.0) @ v[b, h])"),
+    "dropout_renormalised": (
+        "o[b, h, r0:r1] = (np.where(keep, prob, 0.0) @ v[b, h]) * inv_keep",
+        "o[b, h, r0:r1] = (np.where(keep, prob, 0.0) / np.where(keep, prob, 0.0).sum("
+        "axis=1, keepdims=True)) @ v[b, h]"),
+    "dropout_bwd_dp_unmasked": ("dp = (g @ v[b, h].T) * scale_keep", "dp = (g @ v[b, h].T)"),
+    "dropout_bwd_dv_unmasked": ("dv[b, h] += (prob * scale_keep).T @ g", "dv[b, h] += prob.T @ g"),
     "bwd_dk_sign": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
                     "dk[b, h] -= scale * (ds.T @ q[b, h, r0:r1])"),
 }
 
 
-def _load_mutant(name, old, new):
-    with open(SRC) as f:
+# Mistakes planted in the generator and keep-mask module; the oracle under
+# test then draws its dropout bits from the mutated copy.
+RNG_MUTANTS = {
+    "rng_counter_swapped": ("philox4x32_10((cols >> 2)[None, :], (rows >> 2)[:, None],",
+                            "philox4x32_10((rows >> 2)[:, None], (cols >> 2)[None, :],"),
+    "rng_weyl_constant": ("PHILOX_W0 = 0x9E3779B9", "PHILOX_W0 = 0x9E3779B8"),
+    "rng_word_of_row": ("(rows & 3)[None, :, None]", "(3 - (rows & 3))[None, :, None]"),
+    "rng_threshold_truncated": ("math.floor(float(np.float32(p)) * 256.0 + 0.5)",
+                                "math.floor(float(np.float32(p)) * 256.0)"),
+}
+
+
+def _module(name, path, old=None, new=None):
+    with open(path) as f:
         src = f.read()
-    assert src.count(old) >= 1, f"mutant {name}: pattern not found in oracle"
-    src = src.replace(old, new, 1)
+    if old is not None:
+        assert src.count(old) >= 1, f"mutant {name}: pattern not found in {path}"
+        src = src.replace(old, new, 1)
     mod = types.ModuleType(f"oracle_mutant_{name}")
     exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)  # noqa: S102
     return mod
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+def _load_mutant(name, old, new):
+    return _module(name, SRC, old, new)
+
+
+def _load_rng_mutant(name, old, new):
+    mod = _module(name, SRC)
+    mod._rng = _module(name + "_rng", RNG_SRC, old, new)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(RNG_MUTANTS))
 def test_mutant_is_caught(name):
-    mod = _load_mutant(name, *MUTANTS[name])
+    if name in MUTANTS:
+        mod = _load_mutant(name, *MUTANTS[name])
+    else:
+        mod = _load_rng_mutant(name, *RNG_MUTANTS[name])
     caught = []
     for pin in ALL_PINS:
         try:
