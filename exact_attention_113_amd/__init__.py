@@ -50,8 +50,13 @@ def default_scale(D):
     return 1.0 / math.sqrt(D)
 
 
-def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """Fused forward. Returns (o, lse): o like q, lse fp32 [B, H, N] (natural log)."""
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None, dropout_p=0.0, seed=0,
+            offset=0):
+    """Fused forward. Returns (o, lse): o like q, lse fp32 [B, H, N] (natural log).
+
+    dropout_p > 0 drops attention probabilities with counter-based bits keyed by
+    (seed, offset); the same arguments to `backward` regenerate them.
+    """
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
     if scale is None:
@@ -62,10 +67,17 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     lib = _lib.load()
     with torch.cuda.device(q.device):
-        st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, H, N, D, float(scale), int(bool(causal)),
-                            _DTYPES[q.dtype], _stream_handle(q))
-    _lib.check("fa_forward", st)
+        if dropout_p:
+            st = lib.fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), B, H, N, D, float(scale),
+                                        int(bool(causal)), _DTYPES[q.dtype], float(dropout_p),
+                                        int(seed), int(offset), _stream_handle(q))
+            _lib.check("fa_forward_dropout", st)
+        else:
+            st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N, D, float(scale), int(bool(causal)),
+                                _DTYPES[q.dtype], _stream_handle(q))
+            _lib.check("fa_forward", st)
     return out, lse
 
 
@@ -161,8 +173,10 @@ def backward_workspace_bytes(B, H, N, D):
     return int(_lib.load().fa_backward_workspace_bytes(B, H, N, D))
 
 
-def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
-    """Backward from the forward's o and lse. Returns (dq, dk, dv)."""
+def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, dropout_p=0.0,
+             seed=0, offset=0):
+    """Backward from the forward's o and lse (and its dropout arguments).
+    Returns (dq, dk, dv)."""
     _check_qkv(q, k, v)
     for name, t in (("o", o), ("do", do)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
@@ -177,33 +191,40 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     lib = _lib.load()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), B, H, N, D, float(scale), int(bool(causal)), _DTYPES[q.dtype])
     with torch.cuda.device(q.device):
-        st = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                             do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                             dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, D,
-                             float(scale), int(bool(causal)), _DTYPES[q.dtype],
-                             _stream_handle(q))
-    _lib.check("fa_backward", st)
+        if dropout_p:
+            st = lib.fa_backward_dropout(*args, float(dropout_p), int(seed), int(offset),
+                                         _stream_handle(q))
+            _lib.check("fa_backward_dropout", st)
+        else:
+            st = lib.fa_backward(*args, _stream_handle(q))
+            _lib.check("fa_backward", st)
     return dq, dk, dv
 
 
 class _FlashAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal, scale):
-        o, lse = forward(q, k, v, causal, scale)
+    def forward(ctx, q, k, v, causal, scale, dropout_p, seed, offset):
+        o, lse = forward(q, k, v, causal, scale, dropout_p=dropout_p, seed=seed, offset=offset)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.causal, ctx.scale = causal, scale
+        ctx.dropout = (dropout_p, seed, offset)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
-        return dq, dk, dv, None, None
+        p, seed, offset = ctx.dropout
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale,
+                              dropout_p=p, seed=seed, offset=offset)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def attention(q, k, v, causal=False, scale=None):
-    """Autograd-aware fused attention (O only)."""
+def attention(q, k, v, causal=False, scale=None, dropout_p=0.0, seed=0, offset=0):
+    """Autograd-aware fused attention (O only), with optional dropout."""
     if scale is None:
         scale = default_scale(q.shape[-1])
-    return _FlashAttention.apply(q, k, v, causal, scale)
+    return _FlashAttention.apply(q, k, v, causal, scale, dropout_p, seed, offset)

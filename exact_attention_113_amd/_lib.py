@@ -11,10 +11,15 @@ FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP
 
 # Every symbol include/fa.h declares, with (restype, argtypes).
 _P, _I64, _F, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+_U64 = ctypes.c_uint64
 PROTOTYPES = {
     "fa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _I, _I, _P]),
     "fa_forward_varlen": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                          _I64, _F, _I, _I, _P]),
+    "fa_forward_dropout": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _I, _I,
+                                          _F, _U64, _U64, _P]),
+    "fa_backward_dropout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64,
+                                           _I64, _I64, _I64, _F, _I, _I, _F, _U64, _U64, _P]),
     "fa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "fa_decode_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64]),
     "fa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64,

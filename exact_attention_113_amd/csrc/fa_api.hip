@@ -88,23 +88,99 @@ bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWo
 
 }  // namespace fa
 
+namespace {
+
+fa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                       int dtype, void* stream, const fa::DropParams& drop, const char* who) {
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o and lse must be non-NULL", who);
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o must be 16-byte aligned", who);
+  if (misaligned(lse, 4)) return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", who);
+  fa_status s = check_shape(B, H, N, D, scale, dtype);
+  if (s != FA_OK) return s;
+  fa::FwdArgs a{q,     k,      v,     o,     lse, B, H, N, D, scale, causal, dtype, (hipStream_t)stream,
+                H,     nullptr, 0,    drop};
+  return hip_status(fa::launch_forward(a), who);
+}
+
+fa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                        int64_t D, float scale, int causal, int dtype, void* stream,
+                        const fa::DropParams& drop, const char* who) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "%s: q, k, v, o, dout, lse, dq, dk, dv must be non-NULL", who);
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: tensors must be 16-byte aligned", who);
+  if (misaligned(lse, 4)) return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", who);
+  fa_status s = check_shape(B, H, N, D, scale, dtype);
+  if (s != FA_OK) return s;
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: fp32 backward is not supported", who);
+  fa::BwdWorkspace ws;
+  if (!fa::backward_workspace_layout(B, H, N, D, &ws))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace size overflows", who);
+  if (!workspace)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace is NULL (needs %lld bytes)", who,
+                (long long)ws.total);
+  if (workspace_bytes < ws.total)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace too small (needs %lld bytes)", who,
+                (long long)ws.total);
+  if (misaligned(workspace, 256))
+    return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, D, scale, causal, dtype,
+                (hipStream_t)stream, drop};
+  return hip_status(fa::launch_backward(a, ws), who);
+}
+
+// Dropout constants from the caller's probability, seed and offset: the
+// byte threshold floor(256 p + 0.5) (so p is rounded to a multiple of 1/256)
+// and the scale of the kept probabilities 1 / (1 - thr / 256).
+fa_status drop_params(float p, uint64_t seed, uint64_t offset, int dtype, const char* who,
+                      fa::DropParams* out) {
+  if (!(p >= 0.f && p < 1.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: dropout_p must be in [0, 1)", who);
+  const uint32_t thr = (uint32_t)floor((double)p * 256.0 + 0.5);
+  if (thr > 255)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: dropout_p rounds to 1 (must be below 255.5/256)",
+                who);
+  if (offset > 0xffffffffull)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: offset must be below 2^32", who);
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: fp32 is not supported", who);
+  out->thr = thr;
+  out->k0 = (uint32_t)(seed & 0xffffffffu);
+  out->k1 = (uint32_t)(seed >> 32);
+  out->offset = (uint32_t)offset;
+  out->inv_keep = (float)(1.0 / (1.0 - thr / 256.0));
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
 
 fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                      int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
                      void* stream) {
   g_last_error[0] = '\0';
-  if (!q || !k || !v || !o || !lse)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: q, k, v, o and lse must be non-NULL");
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: q, k, v, o must be 16-byte aligned");
-  if (misaligned(lse, 4))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward: lse must be 4-byte aligned");
-  fa_status s = check_shape(B, H, N, D, scale, dtype);
+  return forward_impl(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, stream, fa::DropParams{},
+                      "fa_forward");
+}
+
+fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                             int dtype, float dropout_p, uint64_t seed, uint64_t offset,
+                             void* stream) {
+  g_last_error[0] = '\0';
+  fa::DropParams dp;
+  fa_status s = drop_params(dropout_p, seed, offset, dtype, "fa_forward_dropout", &dp);
   if (s != FA_OK) return s;
-  fa::FwdArgs a{q,     k,      v,     o,     lse, B, H, N, D, scale, causal, dtype, (hipStream_t)stream,
-                H,     nullptr, 0};
-  return hip_status(fa::launch_forward(a), "fa_forward");
+  return forward_impl(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, stream, dp,
+                      "fa_forward_dropout");
 }
 
 fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -155,32 +231,21 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
                       int64_t D, float scale, int causal, int dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
-    return fail(FA_ERR_INVALID_ARGUMENT,
-                "fa_backward: q, k, v, o, dout, lse, dq, dk, dv must be non-NULL");
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
-      misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_backward: tensors must be 16-byte aligned");
-  if (misaligned(lse, 4))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_backward: lse must be 4-byte aligned");
-  fa_status s = check_shape(B, H, N, D, scale, dtype);
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
+                       scale, causal, dtype, stream, fa::DropParams{}, "fa_backward");
+}
+
+fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                              int64_t N, int64_t D, float scale, int causal, int dtype,
+                              float dropout_p, uint64_t seed, uint64_t offset, void* stream) {
+  g_last_error[0] = '\0';
+  fa::DropParams dp;
+  fa_status s = drop_params(dropout_p, seed, offset, dtype, "fa_backward_dropout", &dp);
   if (s != FA_OK) return s;
-  if (dtype == FA_FP32)
-    return fail(FA_ERR_UNSUPPORTED, "fa_backward: fp32 backward is not supported");
-  fa::BwdWorkspace ws;
-  if (!fa::backward_workspace_layout(B, H, N, D, &ws))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_backward: workspace size overflows");
-  if (!workspace)
-    return fail(FA_ERR_WORKSPACE, "fa_backward: workspace is NULL (needs %lld bytes)",
-                (long long)ws.total);
-  if (workspace_bytes < ws.total)
-    return fail(FA_ERR_WORKSPACE, "fa_backward: workspace too small (needs %lld bytes)",
-                (long long)ws.total);
-  if (misaligned(workspace, 256))
-    return fail(FA_ERR_WORKSPACE, "fa_backward: workspace must be 256-byte aligned");
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, D, scale, causal, dtype,
-                (hipStream_t)stream};
-  return hip_status(fa::launch_backward(a, ws), "fa_backward");
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
+                       scale, causal, dtype, stream, dp, "fa_backward_dropout");
 }
 
 const char* fa_status_string(int status) {

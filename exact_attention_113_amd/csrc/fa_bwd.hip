@@ -137,12 +137,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------- dK, dV
 
-template <typename TT, int D, bool CAUSAL>
+template <typename TT, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ DELTA, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int N, int n_ktiles, float c, float dk_scale, uint32_t qsign) {
+    uint16_t* __restrict__ dV, int N, int n_ktiles, float c, float dk_scale, uint32_t qsign,
+    const DropParams drop) {
   constexpr int BK = 128;                // keys per workgroup: 32 per wave pair
   constexpr int BM = 64;                 // query rows per iteration
   constexpr int ROWB = 2 * D;
@@ -242,13 +243,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         p[r] = x;
       }
     }
+    // With dropout, P goes to the partner with its sign bit set where the
+    // element is dropped (P >= 0, so the bit is free), and the dV operand
+    // holds the kept probabilities (dV is scaled by 1 / (1 - p) at the end).
+    float pd[16];
+    if constexpr (DROP) {
+      const uint32_t bits = keep_bits_keys(drop, bh, key, i * BM + 32 * qb, hi, lane & 3);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool kept = (bits >> r) & 1u;
+        pd[r] = kept ? p[r] : 0.f;
+        p[r] = kept ? p[r] : -p[r];  // sign bit set (-0 for a masked 0)
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pd[r] = p[r];
+    }
     f32x4* dst = pex + ((pair * 2 + qb) * 4) * 64 + lane;
 #pragma unroll
     for (int m = 0; m < 4; ++m) dst[64 * m] = f32x4{p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pp[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) pp[h][e] = TT::pack2(pd[8 * h + 2 * e], pd[8 * h + 2 * e + 1]);
   };
 
   // Role B, phase 1: dP = dO V^T for one query block.
@@ -278,7 +295,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const f32x4 p4 = src[64 * m];
       const f32x4 d4 = *(const f32x4*)(st + BM + 32 * qb + 8 * m + 4 * hi);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ds[4 * m + e] = p4[e] * (dp[4 * m + e] - d4[e]);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (DROP) {
+          // dS = P (keep * dP / (1 - p) - delta), the keep bit in P's sign
+          // (a dropped P of 0 reads as kept, which changes nothing since
+          // its dS is 0). Written with float operations: the same steps on
+          // the integer bit pattern were compiled to wrong results.
+          const float pv = fabsf(p4[e]);
+          const float g = p4[e] < 0.f ? 0.f : dp[4 * m + e] * drop.inv_keep;
+          ds[4 * m + e] = pv * (g - d4[e]);
+        } else {
+          ds[4 * m + e] = p4[e] * (dp[4 * m + e] - d4[e]);
+        }
+      }
     }
     u32x4 sp[2];
 #pragma unroll
@@ -352,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // lq holds key kw0 + lq; register r holds dim 32 db + 8(r/4) + 4 hi + r%4.
   if (key < N) {
     uint16_t* out = (role_a ? dV : dK) + head + (size_t)key * D;
-    const float sc = role_a ? 1.f : dk_scale;
+    const float sc = role_a ? (DROP ? drop.inv_keep : 1.f) : dk_scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -367,12 +396,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------- dQ
 
-template <typename TT, int D, bool CAUSAL>
+template <typename TT, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ DELTA, uint16_t* __restrict__ dQ,
-    int N, int n_qtiles, float c, float dq_scale, uint32_t qsign) {
+    int N, int n_qtiles, float c, float dq_scale, uint32_t qsign, const DropParams drop) {
   constexpr int BM = 32 * kWaves;  // query rows per workgroup
   constexpr int BN = 64;           // keys per LDS tile
   constexpr int ROWB = 2 * D;
@@ -447,6 +476,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(vt, 32 * half, lq, hi, kk), gf[kk], dp);
     __builtin_amdgcn_sched_barrier(0);
     float ds[16];
+    uint32_t kept = 0xffffu;
+    if constexpr (DROP) kept = keep_bits_rows(drop, bh, qi, 32 * b, hi, lane & 3);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = fast_exp2(fmaf(s[r], c, -l2));
@@ -455,7 +486,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         const bool ok = kidx < N && (!CAUSAL || kidx <= qi);
         p = ok ? p : 0.f;
       }
-      ds[r] = p * (dp[r] - dl);
+      if constexpr (DROP) {
+        // dS = P (keep * dP / (1 - p) - delta)
+        ds[r] = p * ((((kept >> r) & 1u) ? dp[r] * drop.inv_keep : 0.f) - dl);
+      } else {
+        ds[r] = p * (dp[r] - dl);
+      }
     }
     u32x4 sp[2];
 #pragma unroll
@@ -538,33 +574,27 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   const int bh = (int)(a.B * a.H);
 
   const int n_ktiles = (int)((a.N + 127) / 128);
-  const dim3 g1((unsigned)((int64_t)n_ktiles * bh));
-  if (a.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, true>), g1, dim3(kThreads), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       (int)a.N, n_ktiles, c, dk_scale, qsign);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, false>), g1, dim3(kThreads), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       (int)a.N, n_ktiles, c, dk_scale, qsign);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
   const int n_qtiles = (int)((a.N + 255) / 256);
+  const dim3 g1((unsigned)((int64_t)n_ktiles * bh));
   const dim3 g2((unsigned)((int64_t)n_qtiles * bh));
-  if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, true>), g2, dim3(kThreads), 0, a.stream,
+  auto go = [&](auto causal, auto drop) -> hipError_t {
+    constexpr bool C = decltype(causal)::value, DR = decltype(drop)::value;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, C, DR>), g1, dim3(kThreads), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       (int)a.N, n_ktiles, c, dk_scale, qsign, a.drop);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, C, DR>), g2, dim3(kThreads), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dq, (int)a.N, n_qtiles,
-                       c, dq_scale, qsign);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, false>), g2, dim3(kThreads), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dq, (int)a.N, n_qtiles,
-                       c, dq_scale, qsign);
-  return hipGetLastError();
+                       c, dq_scale, qsign, a.drop);
+    return hipGetLastError();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (a.drop.thr != 0) return a.causal ? go(T_{}, T_{}) : go(F_{}, T_{});
+  return a.causal ? go(T_{}, F_{}) : go(F_{}, F_{});
 }
 
 }  // namespace

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_internal.h"
+
 namespace fa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -89,6 +91,104 @@ __device__ __forceinline__ float half_swap_sum(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// ---- dropout bits -----------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds on a 128-bit counter with a 64-bit
+// key; each round multiplies counter words 0 and 2 by two fixed constants,
+// crosses the high halves into words 1 and 3 with the key, and the key is
+// bumped by two Weyl constants.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+    c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Dropout of element (i, j) of head bh: byte j % 4 of word i % 4 of the
+// Philox call with counter (j / 4, i / 4, bh, offset); dropped when the byte
+// is below thr (thr = floor(256 p + 0.5)).
+// (DropParams, the per-call constants, is declared in fa_internal.h.)
+
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+}
+
+// 4x4 transpose of 32-bit words across the four lanes of a quad: lane s
+// holds row s (x[0..3]) on entry and column s (x[0..3] = rows 0..3 of
+// column s) on return. Two exchanges (lanes s ^ 2, then s ^ 1).
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 x, int s) {
+  const bool b1 = (s & 2) != 0, b0 = (s & 1) != 0;
+  // Stage 1: keep the two columns c with c & 2 == s & 2, swap the others.
+  const uint32_t r0 = quad_xor2(b1 ? x[0] : x[2]);
+  const uint32_t r1 = quad_xor2(b1 ? x[1] : x[3]);
+  const uint32_t own0 = b1 ? x[2] : x[0], own1 = b1 ? x[3] : x[1];  // row s, cols (s&2)+0,1
+  // (r0, r1): row s ^ 2, the same two columns.
+  // Stage 2: keep column s, swap the other one of the pair.
+  const uint32_t q0 = quad_xor1(b0 ? own0 : own1);  // row s ^ 1, column s
+  const uint32_t q1 = quad_xor1(b0 ? r0 : r1);      // row s ^ 3, column s
+  const uint32_t mine = b0 ? own1 : own0;           // row s, column s
+  const uint32_t par = b0 ? r1 : r0;                // row s ^ 2, column s
+  // Rows in order: row k is at relative position k ^ s.
+  u32x4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rel = k ^ s;
+    out[k] = rel == 0 ? mine : rel == 1 ? q0 : rel == 2 ? par : q1;
+  }
+  return out;
+}
+
+// 4x4 transpose of the bytes of four words: byte t of word w becomes byte w
+// of word t.
+__device__ __forceinline__ u32x4 byte_transpose(u32x4 x) {
+  u32x4 out;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    out[t] = ((x[0] >> (8 * t)) & 0xffu) | (((x[1] >> (8 * t)) & 0xffu) << 8) |
+             (((x[2] >> (8 * t)) & 0xffu) << 16) | (((x[3] >> (8 * t)) & 0xffu) << 24);
+  return out;
+}
+
+// Keep bits of the 16 scores a lane holds in the transposed-score layout
+// (lane = one row, register r = key 8 (r / 4) + 4 hi + r % 4 of a 32-key
+// block starting at key0; the four lanes of a quad hold rows 4a .. 4a + 3).
+// Bit r of the result is set when element r is kept. Each lane of the quad
+// computes one of the four calls its rows need.
+__device__ __forceinline__ uint32_t keep_bits_rows(const DropParams& dp, int bh, int row,
+                                                   int key0, int hi, int s) {
+  const u32x4 w = philox4x32_10(
+      u32x4{(uint32_t)((key0 >> 2) + 2 * s + hi), (uint32_t)(row >> 2), (uint32_t)bh, dp.offset},
+      dp.k0, dp.k1);
+  const u32x4 v = quad_transpose(w, s);  // v[m] = word (row % 4) of call m
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bits |= (((v[r >> 2] >> (8 * (r & 3))) & 0xffu) >= dp.thr ? 1u : 0u) << r;
+  return bits;
+}
+
+// The same for the layout with rows in the registers: lane = one key,
+// register r = row 8 (r / 4) + 4 hi + r % 4 of a 32-row block starting at
+// row0; the four lanes of a quad hold keys 4b .. 4b + 3.
+__device__ __forceinline__ uint32_t keep_bits_keys(const DropParams& dp, int bh, int key,
+                                                   int row0, int hi, int s) {
+  const u32x4 w = philox4x32_10(
+      u32x4{(uint32_t)(key >> 2), (uint32_t)((row0 >> 2) + 2 * s + hi), (uint32_t)bh, dp.offset},
+      dp.k0, dp.k1);
+  const u32x4 v = quad_transpose(byte_transpose(w), s);  // v[m] byte e: row 4 m' + e, this key
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bits |= (((v[r >> 2] >> (8 * (r & 3))) & 0xffu) >= dp.thr ? 1u : 0u) << r;
+  return bits;
+}
 
 // Map a linear workgroup id to a logical one so that runs of consecutive
 // logical ids land on one XCD. Workgroups are dealt to the 8 XCDs round

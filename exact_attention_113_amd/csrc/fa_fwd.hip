@@ -110,9 +110,10 @@ struct FwdParams {
   int bh_count;
   float c;
   uint32_t qsign;
+  DropParams drop;    // dense batches only
 };
 
-template <typename TT, int D, bool CAUSAL, int NW>
+template <typename TT, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const FwdParams prm) {
   constexpr int kBM = 32 * NW;                // query rows per workgroup
   constexpr int CH = D / 8;                   // 16-byte chunks per row
@@ -267,6 +268,22 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
       }
   };
 
+  // Dropout on the P V operand only: the row sum (and so LSE) keeps every
+  // probability, the kept ones enter P V unscaled and O is scaled by
+  // 1 / (1 - p) at the end.
+  auto drop_operand = [&](int b, const float (&p)[16], u32x4 (&pf)[2])
+      __attribute__((always_inline)) {
+    const uint32_t bits = keep_bits_rows(prm.drop, bh, qi, kKB * b, hi, lane & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * h + 2 * e;
+        pf[h][e] = TT::pack2(((bits >> r) & 1u) ? p[r] : 0.f,
+                             ((bits >> (r + 1)) & 1u) ? p[r + 1] : 0.f);
+      }
+  };
+
   // Softmax of block b: mask (edge steps), row max, lazy reference update,
   // probabilities packed as the B operands of the P V product, row sum.
   auto softmax_full = [&](auto edge, int b, f32x16& s, u32x4 (&pf)[2])
@@ -312,6 +329,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pf[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+    if constexpr (DROP) drop_operand(b, p, pf);
     rescale = wave_any(need);
   };
 
@@ -343,6 +361,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) pf[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+      if constexpr (DROP) drop_operand(b, p, pf);
       const float lprev = lsum;
       lsum = lprev + sum;
       rescale = false;
@@ -457,7 +476,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
 
   // O = acc / sum rounded to the dtype; LSE = ln 2 * (ref + log2 sum).
   const float ltot = half_swap_sum(lsum);
-  const float inv = 1.f / ltot;
+  const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
   if (qi < N) {
     uint16_t* orow = prm.o + qbase + (size_t)qi * sq;
 #pragma unroll
@@ -489,15 +508,27 @@ hipError_t launch_half(const FwdArgs& a) {
   p.bh_count = (int)(a.B * a.H);
   p.c = fabsf(a.scale) * kLog2e;
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  p.drop = a.drop;
   auto go = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
+    if (a.drop.thr != 0) {
+      p.n_qtiles = (int)((a.N + 32 * NW - 1) / (32 * NW));
+      const int64_t grid = (int64_t)p.n_qtiles * p.bh_count;
+      if (a.causal)
+        hipLaunchKernelGGL((fwd_kernel<TT, D, true, NW, true>), dim3((unsigned)grid),
+                           dim3(64 * NW), 0, a.stream, p);
+      else
+        hipLaunchKernelGGL((fwd_kernel<TT, D, false, NW, true>), dim3((unsigned)grid),
+                           dim3(64 * NW), 0, a.stream, p);
+      return;
+    }
     p.n_qtiles = (int)((a.N + 32 * NW - 1) / (32 * NW));
     const int64_t grid = (int64_t)p.n_qtiles * p.bh_count;
     if (a.causal)
-      hipLaunchKernelGGL((fwd_kernel<TT, D, true, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+      hipLaunchKernelGGL((fwd_kernel<TT, D, true, NW, false>), dim3((unsigned)grid), dim3(64 * NW), 0,
                          a.stream, p);
     else
-      hipLaunchKernelGGL((fwd_kernel<TT, D, false, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+      hipLaunchKernelGGL((fwd_kernel<TT, D, false, NW, false>), dim3((unsigned)grid), dim3(64 * NW), 0,
                          a.stream, p);
   };
   const int64_t bh = a.B * a.H;

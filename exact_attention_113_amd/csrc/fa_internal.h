@@ -8,6 +8,16 @@
 
 namespace fa {
 
+// Attention dropout constants of one call: element (i, j) of head bh is
+// dropped when byte j % 4 of word i % 4 of Philox4x32-10 with counter
+// (j / 4, i / 4, bh, offset) and key (k0, k1) is below thr.
+struct DropParams {
+  uint32_t thr;       // floor(256 p + 0.5); 0 = no dropout
+  uint32_t k0, k1;    // seed, low and high 32 bits
+  uint32_t offset;
+  float inv_keep;     // 1 / (1 - thr / 256)
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -25,6 +35,7 @@ struct FwdArgs {
   int64_t H_kv;
   const int32_t* cu_seqlens;
   int64_t total;
+  DropParams drop;   // thr = 0: none (dense batches only)
 };
 
 struct BwdArgs {
@@ -43,6 +54,7 @@ struct BwdArgs {
   int causal;
   int dtype;
   hipStream_t stream;
+  DropParams drop;   // thr = 0: none
 };
 
 // Byte offsets of the backward workspace's parts (each 256-byte aligned).

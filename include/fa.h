@@ -100,6 +100,35 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
                      int dtype, void* stream);
 
 /*
+ * fa_forward_dropout - fa_forward with dropout on the attention
+ * probabilities (training).
+ *
+ * The dropout branch of "Flash Attention algorithm design and I/O
+ * optimisation" (verification answer), read as the usual attention dropout:
+ * P = softmax(scale * Q K^T [masked]) as in fa_forward (LSE is unchanged),
+ * each P[i][j] kept or dropped by counter-based random bits, and
+ *   O = (P * keep) V / (1 - thr / 256).
+ * Element (i, j) of head bh = b * H + h is dropped when byte j % 4 of word
+ * i % 4 of Philox4x32-10 (Salmon et al., SC 2011) with counter
+ * (j / 4, i / 4, bh, offset) and key (seed mod 2^32, seed / 2^32) is below
+ * thr = floor(256 * dropout_p + 0.5): the probability is rounded to a
+ * multiple of 1/256. The same (seed, offset) in fa_backward_dropout
+ * regenerates the same decisions; nothing is stored.
+ *
+ *   dropout_p  0 <= p < 255.5/256 (thr = 0 is exactly fa_forward)
+ *   seed       any 64-bit value
+ *   offset     below 2^32 (e.g. a per-step counter)
+ *   dtype      FA_FP16 or FA_BF16 (FA_FP32 returns FA_ERR_UNSUPPORTED)
+ *   other arguments as for fa_forward
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                             int dtype, float dropout_p, uint64_t seed, uint64_t offset,
+                             void* stream);
+
+/*
  * fa_forward_varlen - fused attention forward over a packed batch of
  * variable-length sequences, with grouped K/V heads (GQA/MQA).
  *
@@ -178,6 +207,22 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
                       int64_t N, int64_t D, float scale, int causal, int dtype,
                       void* stream);
+
+/*
+ * fa_backward_dropout - backward of fa_forward_dropout: the same dropout
+ * decisions are regenerated from (dropout_p, seed, offset), and
+ *   Pd = P * keep / (1 - p'),  dV = Pd^T dO,
+ *   dP = (dO V^T) * keep / (1 - p'),  delta_i = sum_d dO[i,d] O[i,d],
+ *   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q
+ * (p' = thr / 256). o and lse must come from fa_forward_dropout with the
+ * same arguments. Workspace, arguments and statuses as for fa_backward;
+ * dropout arguments as for fa_forward_dropout. Deterministic (no atomics).
+ */
+fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                              int64_t N, int64_t D, float scale, int causal, int dtype,
+                              float dropout_p, uint64_t seed, uint64_t offset, void* stream);
 
 /*
  * fa_decode_workspace_bytes - device workspace fa_decode needs for these

@@ -304,7 +304,7 @@ def merge_partials(o_parts, lse_parts):
     return o, lse
 
 
-def attention_forward_dropout(q, k, v, scale, causal, p, seed, offset):
+def attention_forward_dropout(q, k, v, scale, causal, p, seed, offset, bh0=0):
     """Exact attention with dropout on the probabilities (fp64).
 
     The dropout branch that the verification answer of "Flash Attention
@@ -314,7 +314,10 @@ def attention_forward_dropout(q, k, v, scale, causal, p, seed, offset):
     dropped by the counter-based bits of oracle.rng.keep_mask, and
         O = (P * keep) V / (1 - p_eff),   p_eff = dropout_threshold(p) / 256.
 
-    q, k, v: [B, H, N, D]. Returns (O, LSE).
+    q, k, v: [B, H, N, D]; bh0 is the flattened (batch, head) index of the
+    first head given (its random bits are those of head bh0 + b * H + h), so
+    that one head of a larger batch can be checked on its own. Returns
+    (O, LSE).
     """
     q, k, v = _check(q, k, v)
     B, H, N, D = q.shape
@@ -330,13 +333,13 @@ def attention_forward_dropout(q, k, v, scale, causal, p, seed, offset):
                 e = np.exp(s - m)
                 l = e.sum(axis=1, keepdims=True)
                 prob = e / l
-                keep = _rng.keep_mask(b * H + h, np.arange(r0, r1), np.arange(N), p, seed, offset)
+                keep = _rng.keep_mask(bh0 + b * H + h, np.arange(r0, r1), np.arange(N), p, seed, offset)
                 o[b, h, r0:r1] = (np.where(keep, prob, 0.0) @ v[b, h]) * inv_keep
                 lse[b, h, r0:r1] = m[:, 0] + np.log(l[:, 0])
     return o, lse
 
 
-def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
+def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset, bh0=0):
     """dQ, dK, dV of attention_forward_dropout for upstream gradient dO (fp64).
 
     With the keep decisions fixed, the forward is a smooth function of
@@ -345,6 +348,7 @@ def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
         Pd = P * keep / (1 - p_eff),  dV = Pd^T dO,
         dP = (dO V^T) * keep / (1 - p_eff),  delta = rowsum(P * dP),
         dS = P * (dP - delta),  dQ = scale * dS K,  dK = scale * dS^T Q.
+    bh0 as for attention_forward_dropout.
     """
     q, k, v = _check(q, k, v)
     do = np.asarray(do, dtype=np.float64)
@@ -363,7 +367,7 @@ def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
                 m = s.max(axis=1, keepdims=True)
                 e = np.exp(s - m)
                 prob = e / e.sum(axis=1, keepdims=True)
-                keep = _rng.keep_mask(b * H + h, np.arange(r0, r1), np.arange(N), p, seed, offset)
+                keep = _rng.keep_mask(bh0 + b * H + h, np.arange(r0, r1), np.arange(N), p, seed, offset)
                 scale_keep = np.where(keep, inv_keep, 0.0)
                 g = do[b, h, r0:r1]
                 dv[b, h] += (prob * scale_keep).T @ g

@@ -195,3 +195,36 @@ def test_decode_workspace_size():
     splits = (n // 4 - 0) // (rows * 129)  # upper bound on the chunk count
     assert 2 <= splits <= 64
     assert lib.fa_decode_workspace_bytes(0, 1, 8, 2, 64, 128) == 0
+
+
+def fwd_drop(p=0.1, seed=1, offset=0, dtype=2, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=2, N=64, D=64, scale=0.125, causal=1)
+    args.update(kw)
+    return _lib.load().fa_forward_dropout(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                          args["B"], args["H"], args["N"], args["D"],
+                                          args["scale"], args["causal"], dtype, p, seed, offset,
+                                          None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=-0.1), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(p=1.0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(p=0.999), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(p=float("nan")), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(offset=1 << 32), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_forward_dropout_validation(kw, status):
+    assert fwd_drop(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_backward_dropout_validation():
+    lib = _lib.load()
+    base = [A] * 9 + [A, 1 << 30, 1, 2, 64, 64, 0.125, 1, 2]
+    assert lib.fa_backward_dropout(*base, 1.5, 0, 0, None) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_backward_dropout(*base, 0.2, 0, 1 << 33, None) == _lib.FA_ERR_INVALID_ARGUMENT
+    base[9] = None
+    assert lib.fa_backward_dropout(*base, 0.2, 0, 0, None) == _lib.FA_ERR_WORKSPACE
