@@ -20,6 +20,7 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_online,
     attention_forward_varlen,
+    attention_backward_varlen,
     attention_decode,
     attention_forward_dropout,
     attention_backward_dropout,

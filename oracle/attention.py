@@ -377,3 +377,43 @@ def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset, bh0=
                 dq[b, h, r0:r1] = scale * (ds @ k[b, h])
                 dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])
     return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_seqlens, scale, causal):
+    """dQ, dK, dV of attention_forward_varlen for upstream gradient dO (fp64).
+
+    Each (sequence, query head) is its own attention problem, so its
+    gradients are those of attention_backward on that sequence's rows; a K/V
+    head serves the query heads h with h // (H // H_kv) equal to it, so its
+    dK and dV are the sums of their contributions (the chain rule through the
+    shared operand).
+
+    q, do: [total, H, D]; k, v: [total, H_kv, D]. Returns dq [total, H, D],
+    dk and dv [total, H_kv, D]; tokens outside every sequence get zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    total, H, D = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (total, H_kv, D) or v.shape != k.shape or do.shape != q.shape or H % H_kv:
+        raise ValueError("need q, do [total, H, D] and k, v [total, H_kv, D] with H_kv | H")
+    group = H // H_kv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 <= s0:
+            continue
+        for h in range(H):
+            hk = h // group
+            gq, gk, gv = attention_backward(q[None, None, s0:s1, h], k[None, None, s0:s1, hk],
+                                            v[None, None, s0:s1, hk], do[None, None, s0:s1, h],
+                                            scale, causal)
+            dq[s0:s1, h] = gq[0, 0]
+            dk[s0:s1, hk] += gk[0, 0]
+            dv[s0:s1, hk] += gv[0, 0]
+    return dq, dk, dv

@@ -371,6 +371,35 @@ def pin_varlen_sequences_independent(orc):
 
 VARLEN_PINS = [pin_varlen_brute_force, pin_varlen_sequences_independent]
 
+def pin_varlen_backward_finite_differences(orc):
+    """The packed, grouped-head backward against central differences of the
+    packed forward (lengths 3, 0, 4; H = 4 over H_kv = 2 and MQA H_kv = 1)."""
+    cu = [0, 3, 3, 7]
+    for H_kv in (2, 1):
+        q = _rand((7, 4, 2), 101)
+        k = _rand((7, H_kv, 2), 102 + H_kv)
+        v = _rand((7, H_kv, 2), 104 + H_kv)
+        g = _rand((7, 4, 2), 106)
+        for causal in (False, True):
+            grads = orc.attention_backward_varlen(q, k, v, g, cu, 0.9, causal)
+            for idx, x in enumerate((q, k, v)):
+                num = np.zeros_like(x)
+                for pos in np.ndindex(x.shape):
+                    xp, xm = x.copy(), x.copy()
+                    xp[pos] += 1e-6
+                    xm[pos] -= 1e-6
+                    ap, am = [q, k, v], [q, k, v]
+                    ap[idx], am[idx] = xp, xm
+                    fp = (orc.attention_forward_varlen(*ap, cu, 0.9, causal)[0] * g).sum()
+                    fm = (orc.attention_forward_varlen(*am, cu, 0.9, causal)[0] * g).sum()
+                    num[pos] = (fp - fm) / 2e-6
+                err = np.abs(num - grads[idx]).max() / max(1.0, np.abs(num).max())
+                assert err < 1e-7, (H_kv, causal, idx, err)
+
+
+VARLEN_BWD_PINS = [pin_varlen_backward_finite_differences]
+
+
 def brute_force_decode(q, kc, vc, lens, scale):
     """Scalar loops for decode: new token t of sequence b sits at position
     L_b - s_q + t and sees cache keys 0 .. L_b - s_q + t; query head h uses
@@ -609,4 +638,5 @@ FORWARD_PINS = [pin_golden_forward, pin_brute_force, pin_online_equals_three_pas
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_grad_sums,
                  pin_constant_v_grads, pin_scale_zero_grads, pin_delta_two_ways,
                  pin_torch_autograd]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS + DECODE_PINS + DROPOUT_PINS
+ALL_PINS = (FORWARD_PINS + BACKWARD_PINS + VARLEN_PINS + VARLEN_BWD_PINS + DECODE_PINS +
+            DROPOUT_PINS)

@@ -67,6 +67,10 @@ MUTANTS = {
         "axis=1, keepdims=True)) @ v[b, h]"),
     "dropout_bwd_dp_unmasked": ("dp = (g @ v[b, h].T) * scale_keep", "dp = (g @ v[b, h].T)"),
     "dropout_bwd_dv_unmasked": ("dv[b, h] += (prob * scale_keep).T @ g", "dv[b, h] += prob.T @ g"),
+    "varlen_bwd_dk_not_summed": ("            dk[s0:s1, hk] += gk[0, 0]",
+                                 "            dk[s0:s1, hk] = gk[0, 0]"),
+    "varlen_bwd_dv_wrong_head": ("            dv[s0:s1, hk] += gv[0, 0]",
+                                 "            dv[s0:s1, h % H_kv] += gv[0, 0]"),
     "bwd_dk_sign": ("dk[b, h] += scale * (ds.T @ q[b, h, r0:r1])",
                     "dk[b, h] -= scale * (ds.T @ q[b, h, r0:r1])"),
 }
