@@ -205,6 +205,56 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, drop
     return dq, dk, dv
 
 
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=None,
+                    workspace=None, out=None):
+    """Backward of forward_varlen from its o and lse [H, total]. Returns
+    (dq [total, H, D], dk, dv [total, H_kv, D]); dk and dv sum over the query
+    heads that share each K/V head. `out` may give the three output tensors
+    (rows of tokens outside every sequence are left as they are)."""
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[0] != k.shape[0] \
+            or q.shape[2] != k.shape[2]:
+        raise ValueError(f"need q [total, H, D] and k, v [total, H_kv, D], got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or \
+            v.dtype != q.dtype:
+        raise TypeError("dtype must be float16 or bfloat16 (all equal)")
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q (shape, dtype)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse),
+                    ("cu_seqlens", cu_seqlens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    total, H, D = q.shape
+    if lse.shape != (H, total) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [H, total]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [batch + 1]")
+    if scale is None:
+        scale = default_scale(D)
+    need = backward_workspace_bytes(1, H, total, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_cuda or \
+                    not t.is_contiguous():
+                raise ValueError(f"{name} must match its input (shape, dtype, contiguous GPU)")
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), cu_seqlens.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), cu_seqlens.numel() - 1, int(max_seqlen),
+                                    total, H, k.shape[1], D, float(scale), int(bool(causal)),
+                                    _DTYPES[q.dtype], _stream_handle(q))
+    _lib.check("fa_backward_varlen", st)
+    return dq, dk, dv
+
+
 class _FlashAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, causal, scale, dropout_p, seed, offset):
@@ -228,3 +278,27 @@ def attention(q, k, v, causal=False, scale=None, dropout_p=0.0, seed=0, offset=0
     if scale is None:
         scale = default_scale(q.shape[-1])
     return _FlashAttention.apply(q, k, v, causal, scale, dropout_p, seed, offset)
+
+
+class _FlashAttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, scale):
+        o, lse = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+        ctx.max_seqlen, ctx.causal, ctx.scale = max_seqlen, causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cu = ctx.saved_tensors
+        dq, dk, dv = backward_varlen(q, k, v, o, lse, do.contiguous(), cu, ctx.max_seqlen,
+                                     ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None):
+    """Autograd-aware fused attention over a packed variable-length batch with
+    grouped K/V heads (O only)."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    return _FlashAttentionVarlen.apply(q, k, v, cu_seqlens, max_seqlen, causal, scale)

@@ -20,6 +20,8 @@ PROTOTYPES = {
                                           _F, _U64, _U64, _P]),
     "fa_backward_dropout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64,
                                            _I64, _I64, _I64, _F, _I, _I, _F, _U64, _U64, _P]),
+    "fa_backward_varlen": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64,
+                                          _I64, _I64, _I64, _I64, _I64, _F, _I, _I, _P]),
     "fa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "fa_decode_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64]),
     "fa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64,

@@ -158,6 +158,29 @@ fa_status drop_params(float p, uint64_t seed, uint64_t offset, int dtype, const 
   return FA_OK;
 }
 
+// Checks common to the packed variable-length entry points.
+fa_status check_varlen(int64_t batch, int64_t max_seqlen, int64_t total, int64_t H, int64_t H_kv,
+                       int64_t D, float scale, int dtype, const char* who) {
+  if (batch < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: batch must be >= 1 (got %lld)", who,
+                (long long)batch);
+  if (H_kv < 1 || H < 1 || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: H (%lld) must be a positive multiple of H_kv (%lld)",
+                who, (long long)H, (long long)H_kv);
+  if (total < 1 || max_seqlen < 1 || max_seqlen > total)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: need 1 <= max_seqlen (%lld) <= total (%lld)", who,
+                (long long)max_seqlen, (long long)total);
+  fa_status s = check_shape(1, H, total, D, scale, dtype);
+  if (s != FA_OK) return s;
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: fp32 is not supported", who);
+  // Query tiles of 128 (forward) or key tiles of 128 (backward) per
+  // (sequence, head).
+  const int64_t wgs = ((max_seqlen + 127) / 128) * batch * H;
+  if (batch > (int64_t)1 << 30 || wgs > (int64_t)0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed one grid", who, (long long)wgs);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,25 +219,9 @@ fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o
   if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
     return fail(FA_ERR_INVALID_ARGUMENT,
                 "fa_forward_varlen: lse and cu_seqlens must be 4-byte aligned");
-  if (batch < 1)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward_varlen: batch must be >= 1 (got %lld)",
-                (long long)batch);
-  if (H_kv < 1 || H < 1 || H % H_kv != 0)
-    return fail(FA_ERR_INVALID_ARGUMENT,
-                "fa_forward_varlen: H (%lld) must be a positive multiple of H_kv (%lld)",
-                (long long)H, (long long)H_kv);
-  if (total < 1 || max_seqlen < 1 || max_seqlen > total)
-    return fail(FA_ERR_INVALID_ARGUMENT,
-                "fa_forward_varlen: need 1 <= max_seqlen (%lld) <= total (%lld)",
-                (long long)max_seqlen, (long long)total);
-  fa_status s = check_shape(1, H, total, D, scale, dtype);
+  fa_status s = check_varlen(batch, max_seqlen, total, H, H_kv, D, scale, dtype,
+                             "fa_forward_varlen");
   if (s != FA_OK) return s;
-  if (dtype == FA_FP32)
-    return fail(FA_ERR_UNSUPPORTED, "fa_forward_varlen: fp32 is not supported");
-  const int64_t wgs = ((max_seqlen + 255) / 256) * batch * H;
-  if (batch > (int64_t)1 << 30 || wgs > (int64_t)0x7fffffff)
-    return fail(FA_ERR_UNSUPPORTED, "fa_forward_varlen: %lld workgroups exceed one grid",
-                (long long)wgs);
   fa::FwdArgs a{q,     k,      v,     o,      lse,        batch, H,     max_seqlen, D,
                 scale, causal, dtype, (hipStream_t)stream, H_kv, cu_seqlens, total};
   return hip_status(fa::launch_forward(a), "fa_forward_varlen");
@@ -246,6 +253,43 @@ fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const
   if (s != FA_OK) return s;
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
                        scale, causal, dtype, stream, dp, "fa_backward_dropout");
+}
+
+fa_status fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes,
+                             int64_t batch, int64_t max_seqlen, int64_t total, int64_t H,
+                             int64_t H_kv, int64_t D, float scale, int causal, int dtype,
+                             void* stream) {
+  g_last_error[0] = '\0';
+  const char* who = "fa_backward_varlen";
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "%s: q, k, v, o, dout, lse, dq, dk, dv and cu_seqlens must be non-NULL", who);
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: tensors must be 16-byte aligned", who);
+  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse and cu_seqlens must be 4-byte aligned", who);
+  fa_status s = check_varlen(batch, max_seqlen, total, H, H_kv, D, scale, dtype, who);
+  if (s != FA_OK) return s;
+  if (total > (int64_t)0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "%s: total (%lld) above 2^31 - 1", who, (long long)total);
+  fa::BwdWorkspace ws;
+  if (!fa::backward_workspace_layout(1, H, total, D, &ws))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace size overflows", who);
+  if (!workspace)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace is NULL (needs %lld bytes)", who,
+                (long long)ws.total);
+  if (workspace_bytes < ws.total)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace too small (needs %lld bytes)", who,
+                (long long)ws.total);
+  if (misaligned(workspace, 256))
+    return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+  fa::BwdArgs a{q,     k,      v,     o,      dout,  lse,       dq,        dk,
+                dv,    workspace, batch, H,     max_seqlen, D,  scale,     causal,
+                dtype, (hipStream_t)stream, fa::DropParams{}, H_kv, cu_seqlens, total};
+  return hip_status(fa::launch_backward(a, ws), who);
 }
 
 const char* fa_status_string(int status) {

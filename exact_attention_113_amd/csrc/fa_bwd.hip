@@ -12,8 +12,10 @@
 // is bitwise reproducible (the "deterministic" option of "FlashAttention in
 // ops-transformer", "Complete operator", holds always):
 //   1. bwd_pre_kernel   delta and LSE*log2(e) for every row.
-//   2. bwd_dkdv_kernel  one workgroup per 128-key tile of one (batch, head),
-//                       iterating over 64-row query tiles that can see it.
+//   2. bwd_dkdv_kernel  one workgroup per 128-key tile of one (sequence,
+//                       K/V head), iterating over the 64-row query tiles
+//                       that can see it, of every query head that shares
+//                       the K/V head (so dK and dV sum over the group).
 //                       Waves are paired on a SIMD: the first of a pair
 //                       computes S = Q K^T and P for its 32 keys and
 //                       accumulates dV^T += dO^T P; the second computes
@@ -21,7 +23,8 @@
 //                       forms dS and accumulates dK^T += Q^T dS. Each wave
 //                       keeps one 32 x D accumulator and one operand tile in
 //                       registers.
-//   3. bwd_dq_kernel    one workgroup per 256-row query tile, streaming the
+//   3. bwd_dq_kernel    one workgroup per 256-row query tile of one
+//                       (sequence, query head), streaming the
 //                       K and V tiles like the forward: S^T = K Q^T and
 //                       dP^T = V dO^T, dS, then dQ^T += K^T dS^T.
 //
@@ -60,12 +63,12 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Direct global->LDS load of 64 rows [row0, row0 + 64) of a [N, D] matrix
-// into dst (rows past N repeat row N-1), each row swizzled by swz. All
-// waves of the workgroup take part.
+// Direct global->LDS load of 64 rows [row0, row0 + 64) of an N-row matrix
+// with `stride` elements between rows into dst (rows past N repeat row N-1),
+// each row swizzled by swz. All waves of the workgroup take part.
 template <int D>
-__device__ __forceinline__ void load_rows64(const uint16_t* Xh, int row0, int N, char* dst, int w,
-                                            int lane) {
+__device__ __forceinline__ void load_rows64(const uint16_t* Xh, size_t stride, int row0, int N,
+                                            char* dst, int w, int lane) {
   constexpr int CH = D / 8, ROWB = 2 * D, RPI = 64 / CH, LPW = 64 / (kWaves * RPI);
   static_assert(LPW >= 1, "tile too small");
 #pragma unroll
@@ -74,7 +77,7 @@ __device__ __forceinline__ void load_rows64(const uint16_t* Xh, int row0, int N,
     const int r = R0 + lane / CH, p = lane % CH;
     const int grow = min(row0 + r, N - 1);
     const int cg = p ^ swz<CH>(r);  // logical chunk stored at position p
-    __builtin_amdgcn_global_load_lds((const void*)(Xh + (size_t)grow * D + cg * 8),
+    __builtin_amdgcn_global_load_lds((const void*)(Xh + (size_t)grow * stride + cg * 8),
                                      (lds_void*)(dst + R0 * ROWB), 16, 0, 0);
   }
 }
@@ -111,15 +114,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ LSE,
                                                       float* __restrict__ delta,
-                                                      float* __restrict__ lse2, int64_t rows) {
+                                                      float* __restrict__ lse2, int64_t rows,
+                                                      int64_t total, int heads) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
   const int part = (int)(gid % TPR);
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 o = *(const u32x4*)(O + row * D + part * 8);
-    const u32x4 g = *(const u32x4*)(dO + row * D + part * 8);
+    // Row of the statistics: (b, h, i) of [B, H, N], or (h, t) of a packed
+    // batch's [H, total], whose O and dO rows are [total, H, D].
+    const int64_t off = total > 0 ? ((row % total) * heads + row / total) * D : row * D;
+    const u32x4 o = *(const u32x4*)(O + off + part * 8);
+    const u32x4 g = *(const u32x4*)(dO + off + part * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc = fmaf(TT::lo(o[i]), TT::lo(g[i]), acc);
@@ -135,15 +142,70 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------- shared
+
+// Arguments of the two main kernels. Dense: Q, O-side tensors [B, H, N, D],
+// K, V [B, H / group, N, D], statistics [B, H, N]. Packed variable-length
+// batch (cu != null): Q [total, H, D], K, V [total, H / group, D],
+// statistics [H, total]; sequence b is tokens [cu[b], cu[b+1]). Query head
+// h reads K/V head h / group in both.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse2;
+  const float* delta;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* cu;
+  int seqlen;        // dense N, or the longest packed sequence
+  int total;         // packed: tokens in the batch
+  int batch;         // sequences
+  int heads, group;  // query heads; query heads per K/V head
+  int n_tiles;       // per sequence: key tiles (dK/dV) or query tiles (dQ)
+  float c;           // |scale| * log2(e)
+  float grad_scale;  // scale, for dK (dK/dV kernel) or dQ (dQ kernel)
+  uint32_t qsign;
+  DropParams drop;   // dense batches only
+};
+
+// Where sequence b's rows are: its length, the element offsets of row 0 of
+// query head h and of K/V head hk, their row strides, and the offset of
+// head h's statistics.
+struct SeqRows {
+  int N;
+  size_t qbase, qstride, kvbase, kvstride, sbase;
+};
+template <int D>
+__device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b, int h, int hk) {
+  SeqRows r;
+  const int hkv = p.heads / p.group;
+  if (p.cu) {
+    const int s0 = min(max(p.cu[b], 0), p.total);
+    const int s1 = min(max(p.cu[b + 1], s0), p.total);
+    r.N = min(s1 - s0, p.seqlen);
+    r.qbase = ((size_t)s0 * p.heads + h) * D;
+    r.qstride = (size_t)p.heads * D;
+    r.kvbase = ((size_t)s0 * hkv + hk) * D;
+    r.kvstride = (size_t)hkv * D;
+    r.sbase = (size_t)h * p.total + s0;
+  } else {
+    r.N = p.seqlen;
+    r.qbase = ((size_t)b * p.heads + h) * (size_t)p.seqlen * D;
+    r.qstride = D;
+    r.kvbase = ((size_t)b * hkv + hk) * (size_t)p.seqlen * D;
+    r.kvstride = D;
+    r.sbase = ((size_t)b * p.heads + h) * (size_t)p.seqlen;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- dK, dV
 
 template <typename TT, int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE2, const float* __restrict__ DELTA, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int N, int n_ktiles, float c, float dk_scale, uint32_t qsign,
-    const DropParams drop) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams prm) {
   constexpr int BK = 128;                // keys per workgroup: 32 per wave pair
   constexpr int BM = 64;                 // query rows per iteration
   constexpr int ROWB = 2 * D;
@@ -165,16 +227,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int pair = w & 3;
   const bool role_a = w < 4;  // S, P, dV; the other wave of the pair: dP, dS, dK
 
-  // Key tiles with the most query tiles first; heads pinned to XCDs.
+  const float c = prm.c;
+  const uint32_t qsign = prm.qsign;
+  const DropParams& drop = prm.drop;
+  // One (sequence b, K/V head hk, key tile): key tiles with the most query
+  // tiles first, heads pinned to XCDs. Units run head-major, so that each
+  // XCD's share holds every sequence of a few heads (sequences of unequal
+  // length would otherwise load the XCDs unevenly). The group's query heads
+  // all contribute to this tile's dK and dV.
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / n_ktiles;
-  const int kt = logical % n_ktiles;
+  const int unit = logical / prm.n_tiles;
+  const int kt = logical % prm.n_tiles;
+  const int hk = unit / prm.batch, bidx = unit - hk * prm.batch;
+  const SeqRows sr0 = seq_rows<D>(prm, bidx, hk * prm.group, hk);
+  const int N = sr0.N;
   const int k0 = kt * BK;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* dOh = dO + head;
-  const float* lse2h = LSE2 + (size_t)bh * N;
-  const float* delh = DELTA + (size_t)bh * N;
+  if (k0 >= N) return;  // a key tile past the end of a shorter sequence
 
   // This pair's 32 keys as the B operand of S = Q K^T (role A) or of
   // dP = dO V^T (role B): lane (key lq, half hi), k-step kk -> row[16kk + 8hi ..].
@@ -182,11 +250,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int key = kw0 + lq;
   u32x4 bf[KK];
   {
-    const uint16_t* Xh = (role_a ? K : V) + head;
+    const uint16_t* Xh = (role_a ? prm.k : prm.v) + sr0.kvbase;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < N) x = *(const u32x4*)(Xh + (size_t)key * D + 16 * kk + 8 * hi);
+      if (key < N) x = *(const u32x4*)(Xh + (size_t)key * sr0.kvstride + 16 * kk + 8 * hi);
       // K sign-flipped for negative scale: S = Q (-K)^T (exact).
       bf[kk] = role_a ? (x ^ qsign) : x;
     }
@@ -199,17 +267,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const int nq = (N + BM - 1) / BM;
   const int i_begin = CAUSAL ? (k0 / BM) : 0;
+  // Work items u = g * nqg + (i - i_begin): query head hk * group + g, query
+  // tile i, so that one loop covers every query row of the group.
+  const int nqg = nq - i_begin;
+  const int n_items = prm.group * nqg;
+  auto item_head = [&] __device__ (int u) __attribute__((always_inline)) {
+    return hk * prm.group + u / nqg;
+  };
+  auto item_tile = [&] __device__ (int u) __attribute__((always_inline)) {
+    return i_begin + u % nqg;
+  };
 
-  // Query tile i: Q and dO rows go straight to LDS; threads 0..127 fetch
-  // the tile's lse2 (0..63) and delta (64..127) values into a register,
-  // stored to LDS by store_stats once this iteration's reads are done.
-  auto load_qtile = [&] __device__ (int i, char* qd, char* gd) __attribute__((always_inline)) {
-    load_rows64<D>(Qh, i * BM, N, qd, w, lane);
-    load_rows64<D>(dOh, i * BM, N, gd, w, lane);
+  // Item u: Q and dO rows go straight to LDS; threads 0..127 fetch the
+  // tile's lse2 (0..63) and delta (64..127) values into a register, stored
+  // to LDS by store_stats once this iteration's reads are done.
+  auto load_qtile = [&] __device__ (int u, char* qd, char* gd) __attribute__((always_inline)) {
+    const int h = item_head(u), i = item_tile(u);
+    const SeqRows sr = seq_rows<D>(prm, bidx, h, hk);
+    load_rows64<D>(prm.q + sr.qbase, sr.qstride, i * BM, N, qd, w, lane);
+    load_rows64<D>(prm.dout + sr.qbase, sr.qstride, i * BM, N, gd, w, lane);
     float v = 0.f;
     if (tid < 2 * BM) {
       const int row = min(i * BM + (tid & (BM - 1)), N - 1);
-      v = tid < BM ? lse2h[row] : delh[row];
+      v = tid < BM ? prm.lse2[sr.sbase + row] : prm.delta[sr.sbase + row];
     }
     return v;
   };
@@ -219,8 +299,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   // Role A, phase 1: S = Q K^T for one 32-row query block, P (masked),
   // P to LDS for the pair, P packed as the B operand of dV^T += dO^T P.
-  auto phase_a1 = [&] __device__ (auto masked, int i, const char* qt, const float* st, int qb,
-                      u32x4 (&pp)[2]) __attribute__((always_inline)) {
+  auto phase_a1 = [&] __device__ (auto masked, int i, int h, const char* qt, const float* st,
+                                  int qb, u32x4 (&pp)[2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
     f32x16 s;
 #pragma unroll
@@ -248,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // holds the kept probabilities (dV is scaled by 1 / (1 - p) at the end).
     float pd[16];
     if constexpr (DROP) {
-      const uint32_t bits = keep_bits_keys(drop, bh, key, i * BM + 32 * qb, hi, lane & 3);
+      const uint32_t bits =
+          keep_bits_keys(drop, bidx * prm.heads + h, key, i * BM + 32 * qb, hi, lane & 3);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool kept = (bits >> r) & 1u;
@@ -322,17 +403,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   };
 
   // One query tile of one role: phase 1, barrier (P visible), phase 2.
-  auto iteration = [&] __device__ (auto is_a, int i, const char* qt, const char* gt, const float* st)
+  auto iteration = [&] __device__ (auto is_a, int u, const char* qt, const char* gt, const float* st)
       __attribute__((always_inline)) {
     if constexpr (decltype(is_a)::value) {
+      const int i = item_tile(u), h = item_head(u);
       const bool masked = (CAUSAL && i * BM < k0 + BK) || (i * BM + BM > N) || (k0 + BK > N);
       u32x4 pp[2][2];
       if (masked) {
-        phase_a1(std::true_type{}, i, qt, st, 0, pp[0]);
-        phase_a1(std::true_type{}, i, qt, st, 1, pp[1]);
+        phase_a1(std::true_type{}, i, h, qt, st, 0, pp[0]);
+        phase_a1(std::true_type{}, i, h, qt, st, 1, pp[1]);
       } else {
-        phase_a1(std::false_type{}, i, qt, st, 0, pp[0]);
-        phase_a1(std::false_type{}, i, qt, st, 1, pp[1]);
+        phase_a1(std::false_type{}, i, h, qt, st, 0, pp[0]);
+        phase_a1(std::false_type{}, i, h, qt, st, 1, pp[1]);
       }
       __syncthreads();
       phase_a2(gt, 0, pp[0]);
@@ -353,22 +435,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // tile's buffers and the P exchange area. The two roles run separate
   // copies of the loop with the same barriers.
   auto run = [&] __device__ (auto is_a) __attribute__((always_inline)) {
-    if (i_begin < nq) {
-      store_stats(st0, load_qtile(i_begin, qt0, gt0));
+    if (n_items > 0) {
+      store_stats(st0, load_qtile(0, qt0, gt0));
       wait_vmem();
       __syncthreads();
     }
-    for (int i = i_begin; i < nq; i += 2) {
+    for (int u = 0; u < n_items; u += 2) {
       float v1 = 0.f;
-      if (i + 1 < nq) v1 = load_qtile(i + 1, qt1, gt1);
-      iteration(is_a, i, qt0, gt0, st0);
+      if (u + 1 < n_items) v1 = load_qtile(u + 1, qt1, gt1);
+      iteration(is_a, u, qt0, gt0, st0);
       store_stats(st1, v1);
       wait_vmem();
       __syncthreads();
-      if (i + 1 >= nq) break;
+      if (u + 1 >= n_items) break;
       float v0 = 0.f;
-      if (i + 2 < nq) v0 = load_qtile(i + 2, qt0, gt0);
-      iteration(is_a, i + 1, qt1, gt1, st1);
+      if (u + 2 < n_items) v0 = load_qtile(u + 2, qt0, gt0);
+      iteration(is_a, u + 1, qt1, gt1, st1);
       store_stats(st0, v0);
       wait_vmem();
       __syncthreads();
@@ -380,8 +462,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // dK = scale * acc (role B), dV = acc (role A), rounded to the dtype. Lane
   // lq holds key kw0 + lq; register r holds dim 32 db + 8(r/4) + 4 hi + r%4.
   if (key < N) {
-    uint16_t* out = (role_a ? dV : dK) + head + (size_t)key * D;
-    const float sc = role_a ? (DROP ? drop.inv_keep : 1.f) : dk_scale;
+    uint16_t* out = (role_a ? prm.dv : prm.dk) + sr0.kvbase + (size_t)key * sr0.kvstride;
+    const float sc = role_a ? (DROP ? drop.inv_keep : 1.f) : prm.grad_scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -397,11 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------- dQ
 
 template <typename TT, int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE2, const float* __restrict__ DELTA, uint16_t* __restrict__ dQ,
-    int N, int n_qtiles, float c, float dq_scale, uint32_t qsign, const DropParams drop) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm) {
   constexpr int BM = 32 * kWaves;  // query rows per workgroup
   constexpr int BN = 64;           // keys per LDS tile
   constexpr int ROWB = 2 * D;
@@ -416,14 +494,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 31, hi = lane >> 5;
-  // Heaviest causal query tiles first; heads pinned to XCDs.
+  const float c = prm.c;
+  const float dq_scale = prm.grad_scale;
+  const uint32_t qsign = prm.qsign;
+  const DropParams& drop = prm.drop;
+  // One (sequence b, query head h, query tile): heaviest causal query tiles
+  // first, heads pinned to XCDs, units head-major as in the dK/dV kernel.
+  // Head h reads K/V head h / group.
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / n_qtiles;
-  const int qt = n_qtiles - 1 - logical % n_qtiles;
+  const int unit = logical / prm.n_tiles;
+  const int qt = prm.n_tiles - 1 - logical % prm.n_tiles;
+  const int h = unit / prm.batch, bidx = unit - h * prm.batch;
+  const int bh = bidx * prm.heads + h;
+  const SeqRows sr = seq_rows<D>(prm, bidx, h, h / prm.group);
+  const int N = sr.N;
   const int q0 = qt * BM;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  if (q0 >= N) return;  // a query tile past the end of a shorter sequence
+  const uint16_t* Kh = prm.k + sr.kvbase;
+  const uint16_t* Vh = prm.v + sr.kvbase;
 
   // This wave's 32 rows of Q (sign-flipped for negative scale) and dO as B
   // operands of S^T = K Q^T and dP^T = V dO^T, and the rows' statistics.
@@ -434,14 +522,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   for (int kk = 0; kk < KK; ++kk) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (qi < N) {
-      x = *(const u32x4*)(Q + head + (size_t)qi * D + 16 * kk + 8 * hi);
-      y = *(const u32x4*)(dO + head + (size_t)qi * D + 16 * kk + 8 * hi);
+      x = *(const u32x4*)(prm.q + sr.qbase + (size_t)qi * sr.qstride + 16 * kk + 8 * hi);
+      y = *(const u32x4*)(prm.dout + sr.qbase + (size_t)qi * sr.qstride + 16 * kk + 8 * hi);
     }
     qf[kk] = x ^ qsign;
     gf[kk] = y;
   }
-  const float l2 = qi < N ? LSE2[(size_t)bh * N + qi] : 0.f;
-  const float dl = qi < N ? DELTA[(size_t)bh * N + qi] : 0.f;
+  const float l2 = qi < N ? prm.lse2[sr.sbase + qi] : 0.f;
+  const float dl = qi < N ? prm.delta[sr.sbase + qi] : 0.f;
 
   f32x16 acc[DB];  // dQ^T: lane = query, register = dim
 #pragma unroll
@@ -510,14 +598,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     else block(std::false_type{}, b, kt, vt);
   };
 
-  load_rows64<D>(Kh, 0, N, kb0, w, lane);
-  load_rows64<D>(Vh, 0, N, vb0, w, lane);
+  load_rows64<D>(Kh, sr.kvstride, 0, N, kb0, w, lane);
+  load_rows64<D>(Vh, sr.kvstride, 0, N, vb0, w, lane);
   wait_vmem();
   __syncthreads();
   for (int t = 0; t < ntile; t += 2) {
     if (t + 1 < ntile) {
-      load_rows64<D>(Kh, (t + 1) * BN, N, kb1, w, lane);
-      load_rows64<D>(Vh, (t + 1) * BN, N, vb1, w, lane);
+      load_rows64<D>(Kh, sr.kvstride, (t + 1) * BN, N, kb1, w, lane);
+      load_rows64<D>(Vh, sr.kvstride, (t + 1) * BN, N, vb1, w, lane);
     }
     any_block(2 * t, kb0, vb0);
     any_block(2 * t + 1, kb0, vb0);
@@ -525,8 +613,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     __syncthreads();
     if (t + 1 >= ntile) break;
     if (t + 2 < ntile) {
-      load_rows64<D>(Kh, (t + 2) * BN, N, kb0, w, lane);
-      load_rows64<D>(Vh, (t + 2) * BN, N, vb0, w, lane);
+      load_rows64<D>(Kh, sr.kvstride, (t + 2) * BN, N, kb0, w, lane);
+      load_rows64<D>(Vh, sr.kvstride, (t + 2) * BN, N, vb0, w, lane);
     }
     any_block(2 * t + 2, kb1, vb1);
     any_block(2 * t + 3, kb1, vb1);
@@ -537,7 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   // dQ = scale * acc, rounded to the dtype: lane lq holds query qi; register
   // r holds dim 32 db + 8(r/4) + 4 hi + r%4.
   if (qi < N) {
-    uint16_t* out = dQ + head + (size_t)qi * D;
+    uint16_t* out = prm.dq + sr.qbase + (size_t)qi * sr.qstride;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -555,12 +643,13 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   char* wsb = (char*)a.workspace;
   float* delta = (float*)(wsb + ws.delta_off);
   float* lse2 = (float*)(wsb + ws.lse2_off);
-  const int64_t rows = a.B * a.H * a.N;
+  const bool packed = a.cu_seqlens != nullptr;
+  const int64_t rows = packed ? a.H * a.total : a.B * a.H * a.N;
 
   const int64_t pre_threads = rows * (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<TT, D>), dim3((unsigned)((pre_threads + 255) / 256)),
                      dim3(256), 0, a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
-                     delta, lse2, rows);
+                     delta, lse2, rows, packed ? a.total : (int64_t)0, (int)a.H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -569,26 +658,42 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   // For scale < 0 the scores are formed from -K (dK/dV kernel) or -Q (dQ
   // kernel) with |scale|; the gradients dK = scale dS^T Q and dQ = scale dS K
   // use the unflipped operands.
-  const float dk_scale = a.scale;
-  const float dq_scale = a.scale;
-  const int bh = (int)(a.B * a.H);
+  const int64_t hkv = a.H_kv > 0 ? a.H_kv : a.H;
+  BwdParams prm{};
+  prm.q = (const uint16_t*)a.q;
+  prm.k = (const uint16_t*)a.k;
+  prm.v = (const uint16_t*)a.v;
+  prm.dout = (const uint16_t*)a.dout;
+  prm.lse2 = lse2;
+  prm.delta = delta;
+  prm.dq = (uint16_t*)a.dq;
+  prm.dk = (uint16_t*)a.dk;
+  prm.dv = (uint16_t*)a.dv;
+  prm.cu = a.cu_seqlens;
+  prm.seqlen = (int)a.N;
+  prm.total = packed ? (int)a.total : 0;
+  prm.batch = (int)a.B;
+  prm.heads = (int)a.H;
+  prm.group = (int)(a.H / hkv);
+  prm.c = c;
+  prm.grad_scale = a.scale;
+  prm.qsign = qsign;
+  prm.drop = a.drop;
 
   const int n_ktiles = (int)((a.N + 127) / 128);
   const int n_qtiles = (int)((a.N + 255) / 256);
-  const dim3 g1((unsigned)((int64_t)n_ktiles * bh));
-  const dim3 g2((unsigned)((int64_t)n_qtiles * bh));
+  const dim3 g1((unsigned)((int64_t)n_ktiles * a.B * hkv));
+  const dim3 g2((unsigned)((int64_t)n_qtiles * a.B * a.H));
   auto go = [&](auto causal, auto drop) -> hipError_t {
     constexpr bool C = decltype(causal)::value, DR = decltype(drop)::value;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, C, DR>), g1, dim3(kThreads), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       (int)a.N, n_ktiles, c, dk_scale, qsign, a.drop);
+    BwdParams p1 = prm;
+    p1.n_tiles = n_ktiles;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, C, DR>), g1, dim3(kThreads), 0, a.stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, C, DR>), g2, dim3(kThreads), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, lse2, delta, (uint16_t*)a.dq, (int)a.N, n_qtiles,
-                       c, dq_scale, qsign, a.drop);
+    BwdParams p2 = prm;
+    p2.n_tiles = n_qtiles;
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, C, DR>), g2, dim3(kThreads), 0, a.stream, p2);
     return hipGetLastError();
   };
   using T_ = std::true_type;

@@ -55,6 +55,11 @@ struct BwdArgs {
   int dtype;
   hipStream_t stream;
   DropParams drop;   // thr = 0: none
+  // Packed variable-length batch, as in FwdArgs: B sequences given by
+  // cu_seqlens, N = the longest, total = tokens; H_kv divides H (0: H).
+  int64_t H_kv;
+  const int32_t* cu_seqlens;
+  int64_t total;
 };
 
 // Byte offsets of the backward workspace's parts (each 256-byte aligned).

@@ -225,6 +225,40 @@ fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const
                               float dropout_p, uint64_t seed, uint64_t offset, void* stream);
 
 /*
+ * fa_backward_varlen - backward of fa_forward_varlen: the gradients of a
+ * packed batch of variable-length sequences with grouped K/V heads.
+ *
+ * Per (sequence, query head) the formulas of fa_backward hold. A K/V head
+ * is shared by the H / H_kv query heads h with h / (H / H_kv) equal to it,
+ * so its dK and dV are the sums of their contributions (the chain rule
+ * through the shared operand). No step uses atomics: the sums are taken in
+ * a fixed order and the result is bitwise reproducible.
+ *
+ *   q, o, dout  in   [total, H, D] of `dtype`; o from fa_forward_varlen
+ *   k, v        in   [total, H_kv, D] of `dtype`
+ *   lse         in   [H, total] fp32 from fa_forward_varlen
+ *   dq          out  [total, H, D] of `dtype`
+ *   dk, dv      out  [total, H_kv, D] of `dtype`
+ *   cu_seqlens, batch, max_seqlen, total, H, H_kv, D, scale, causal, stream
+ *               as for fa_forward_varlen (same values); rows of tokens not
+ *               covered by any sequence are not written
+ *   workspace   device scratch of at least
+ *               fa_backward_workspace_bytes(1, H, total, D) bytes, owned by
+ *               the caller, 256-byte aligned; contents on entry ignored, on
+ *               return unspecified
+ *   dtype       FA_FP16 or FA_BF16 (FA_FP32 returns FA_ERR_UNSUPPORTED)
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED,
+ * FA_ERR_WORKSPACE or FA_ERR_HIP.
+ */
+fa_status fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes,
+                             int64_t batch, int64_t max_seqlen, int64_t total, int64_t H,
+                             int64_t H_kv, int64_t D, float scale, int causal, int dtype,
+                             void* stream);
+
+/*
  * fa_decode_workspace_bytes - device workspace fa_decode needs for these
  * sizes: per-chunk partial results (fp32 O and LSE of every output row for
  * every key chunk) when the cache is cut into more than one chunk, else 0.

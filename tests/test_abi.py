@@ -152,6 +152,42 @@ def test_forward_varlen_validation(kw, status):
     assert _lib.last_error() != ""
 
 
+def bwd_varlen(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, cu=A, ws=A, ws_bytes=1 << 20,
+               batch=2, max_seqlen=8, total=16, H=4, H_kv=2, D=64, scale=0.125, causal=1,
+               dtype=2):
+    return _lib.load().fa_backward_varlen(q, k, v, o, do, lse, dq, dk, dv, cu, ws, ws_bytes, batch,
+                                          max_seqlen, total, H, H_kv, D, scale, causal, dtype,
+                                          None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(dk=A + 8), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(cu=A + 2), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H=6, H_kv=4), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen=17), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(D=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), _lib.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=256), _lib.FA_ERR_WORKSPACE),
+    (dict(ws=A + 16), _lib.FA_ERR_WORKSPACE),
+])
+def test_backward_varlen_validation(kw, status):
+    assert bwd_varlen(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_backward_varlen_workspace_is_two_stat_rows_per_head_and_token():
+    """The packed backward's workspace is that of a dense batch of one
+    sequence of `total` tokens: fp32 [H, total] twice, each padded."""
+    lib = _lib.load()
+    H, total = 4, 16
+    assert lib.fa_backward_workspace_bytes(1, H, total, 64) == 2 * 256
+    assert bwd_varlen(ws_bytes=2 * 256 - 1, H=H, total=total) == _lib.FA_ERR_WORKSPACE
+
+
 def dec(q=A, k=A, v=A, lens=A, o=A, lse=A, ws=A, ws_bytes=1 << 30, batch=2, s_q=1, cap=64,
         max_len=64, H=8, H_kv=2, D=128, scale=0.125, dtype=2):
     return _lib.load().fa_decode(q, k, v, lens, o, lse, ws, ws_bytes, batch, s_q, cap, max_len,

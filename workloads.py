@@ -135,6 +135,11 @@ class VarlenWorkload:
         f = sum(4.0 * self.H * n * n * self.D for n in self.lengths)
         return f / 2 if self.causal else f
 
+    def flops_bwd(self):
+        """Five n x n x D products per sequence and head (S, dP, dV, dQ, dK):
+        2.5 times the forward's."""
+        return 2.5 * self.flops_fwd()
+
     def bytes_fwd(self):
         esize = torch.empty((), dtype=self.torch_dtype).element_size()
         t = self.total
@@ -152,16 +157,21 @@ def varlen_gqa():
                           32, 8, 128, "bf16", True, 4)
 
 
-def make_varlen_inputs(w: VarlenWorkload, device="cpu"):
+def make_varlen_inputs(w: VarlenWorkload, device="cpu", grad=False):
     """Packed q [total, H, D], k, v [total, H_kv, D] from one generator seeded
-    with w.seed (drawn in the order q, k, v), and cu_seqlens as int32."""
+    with w.seed (drawn in the order q, k, v), and cu_seqlens as int32. With
+    grad=True an upstream gradient dO [total, H, D], drawn after v, comes
+    last."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed)
     q = torch.randn((w.total, w.H, w.D), generator=g).to(w.torch_dtype)
     k = torch.randn((w.total, w.H_kv, w.D), generator=g).to(w.torch_dtype)
     v = torch.randn((w.total, w.H_kv, w.D), generator=g).to(w.torch_dtype)
     cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32)
-    return q.to(device), k.to(device), v.to(device), cu.to(device)
+    out = [q.to(device), k.to(device), v.to(device), cu.to(device)]
+    if grad:
+        out.append(torch.randn((w.total, w.H, w.D), generator=g).to(w.torch_dtype).to(device))
+    return tuple(out)
 
 
 @dataclass(frozen=True)
