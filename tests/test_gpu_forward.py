@@ -145,3 +145,44 @@ def test_autograd_forward_matches():
     o = fa.attention(q, k, v, causal=True)
     o2, _ = run(q, k, v, True, 0.125)
     assert torch.equal(o, o2)
+
+
+def test_long_sequence_sampled_rows():
+    """A 131072-token causal sequence (two heads, D = 128): the last query
+    tile streams 2048 key tiles. Sampled rows are checked against the
+    oracle's definition, row i being the attention of query i over keys
+    0..i."""
+    import oracle.attention as orc
+    B, H, N, D = 1, 2, 131072, 128
+    q, k, v = workloads.make_random((B, H, N, D), seed=77, dtype="bf16", device=DEV)
+    o, lse = run(q, k, v, True, D ** -0.5)
+    for h, i in [(0, 0), (0, 255), (1, 256), (1, 65535), (0, 100003), (1, N - 1)]:
+        # Query i against a cache of its i + 1 visible keys (one new token).
+        ro, rl = orc.attention_decode(to64(q[0, h, i:i + 1])[None, :, None],
+                                      to64(k[0, h, :i + 1])[None, :, None],
+                                      to64(v[0, h, :i + 1])[None, :, None], [i + 1], D ** -0.5)
+        assert_close(f"head {h} row {i} O", to64(o[0, h, i]), ro[0, 0, 0], "bf16", strict=True)
+        assert_lse_close(f"head {h} row {i}", to64(lse[0, h, i:i + 1]), rl[0, 0])
+
+
+def test_offsets_beyond_2g_elements():
+    """4096 sequences x 32 heads of 128 tokens (D = 128): each tensor holds
+    2^31 elements, so the last heads start past 32-bit element offsets.
+    Forward and backward of sampled heads against the oracle. The inputs are
+    drawn on the device from a seeded generator (4 GiB each)."""
+    from gpu_util import oracle_backward
+    B, H, N, D = 4096, 32, 128, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(99)
+    q, k, v, do = (torch.randn((B, H, N, D), generator=g, device=DEV).to(torch.bfloat16)
+                   for _ in range(4))
+    o, lse = fa.forward(q, k, v, causal=True)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (2048, 5), (4095, 31)]
+    ro, rl = oracle_forward(q, k, v, D ** -0.5, True, heads)
+    assert_close("O", pick(o, heads), ro, "bf16", strict=True)
+    assert_lse_close("LSE", pick(lse, heads), rl)
+    for tag, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv),
+                           oracle_backward(q, k, v, do, D ** -0.5, True, heads)):
+        assert_close(tag, pick(got, heads), r, "bf16")
