@@ -169,6 +169,7 @@ struct BwdParams {
   float grad_scale;  // scale, for dK (dK/dV kernel) or dQ (dQ kernel)
   uint32_t qsign;
   DropParams drop;   // dense batches only
+  int diag;          // query i sees keys 0 .. i + diag (0: causal; >= N: all)
 };
 
 // Where sequence b's rows are: its length, the element offsets of row 0 of
@@ -204,7 +205,7 @@ __device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b, int h, in
 
 // ---------------------------------------------------------------- dK, dV
 
-template <typename TT, int D, bool CAUSAL, bool DROP>
+template <typename TT, int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams prm) {
   constexpr int BK = 128;                // keys per workgroup: 32 per wave pair
   constexpr int BM = 64;                 // query rows per iteration
@@ -266,7 +267,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   const int nq = (N + BM - 1) / BM;
-  const int i_begin = CAUSAL ? (k0 / BM) : 0;
+  // The first query tile with a row that sees key k0.
+  const int i_begin = max(0, k0 - prm.diag) / BM;
   // Work items u = g * nqg + (i - i_begin): query head hk * group + g, query
   // tile i, so that one loop covers every query row of the group.
   const int nqg = nq - i_begin;
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
         float x = fast_exp2(fmaf(s[r], c, -l4[e]));
         if (MASK) {
           const int q = i * BM + 32 * qb + 8 * m + 4 * hi + e;
-          const bool ok = q < N && key < N && (!CAUSAL || key <= q);
+          const bool ok = q < N && key < N && key <= q + prm.diag;
           x = ok ? x : 0.f;
         }
         p[r] = x;
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
       __attribute__((always_inline)) {
     if constexpr (decltype(is_a)::value) {
       const int i = item_tile(u), h = item_head(u);
-      const bool masked = (CAUSAL && i * BM < k0 + BK) || (i * BM + BM > N) || (k0 + BK > N);
+      const bool masked = (i * BM + prm.diag < k0 + BK) || (i * BM + BM > N) || (k0 + BK > N);
       u32x4 pp[2][2];
       if (masked) {
         phase_a1(std::true_type{}, i, h, qt, st, 0, pp[0]);
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 
 // ---------------------------------------------------------------- dQ
 
-template <typename TT, int D, bool CAUSAL, bool DROP>
+template <typename TT, int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm) {
   constexpr int BM = 32 * kWaves;  // query rows per workgroup
   constexpr int BN = 64;           // keys per LDS tile
@@ -537,12 +539,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int kv_end = min(N, q0 + BM + prm.diag);
   const int ntile = (kv_end + BN - 1) / BN;
-  const int wave_end = CAUSAL ? min(N, qw0 + 32) : N;
+  const int wave_end = min(N, qw0 + 32 + prm.diag);
   const int last_b = qw0 < N ? (wave_end - 1) / 32 : -1;  // last 32-key block of this wave
   int first_edge = (N % 32) ? (N - 1) / 32 : (kv_end + 31) / 32;
-  if (CAUSAL) first_edge = min(first_edge, qw0 / 32);
+  first_edge = min(first_edge, (qw0 + prm.diag) / 32);
 
   // One 32-key block (half of the tile in kt/vt).
   auto block = [&] __device__ (auto masked, int b, const char* kt, const char* vt)
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
       float p = fast_exp2(fmaf(s[r], c, -l2));
       if (MASK) {
         const int kidx = 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const bool ok = kidx < N && (!CAUSAL || kidx <= qi);
+        const bool ok = kidx < N && kidx <= qi + prm.diag;
         p = ok ? p : 0.f;
       }
       if constexpr (DROP) {
@@ -684,22 +686,22 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   const int n_qtiles = (int)((a.N + 255) / 256);
   const dim3 g1((unsigned)((int64_t)n_ktiles * a.B * hkv));
   const dim3 g2((unsigned)((int64_t)n_qtiles * a.B * a.H));
-  auto go = [&](auto causal, auto drop) -> hipError_t {
-    constexpr bool C = decltype(causal)::value, DR = decltype(drop)::value;
+  prm.diag = a.causal ? 0 : (int)a.N;
+  auto go = [&](auto drop) -> hipError_t {
+    constexpr bool DR = decltype(drop)::value;
     BwdParams p1 = prm;
     p1.n_tiles = n_ktiles;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, C, DR>), g1, dim3(kThreads), 0, a.stream, p1);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR>), g1, dim3(kThreads), 0, a.stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     BwdParams p2 = prm;
     p2.n_tiles = n_qtiles;
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, C, DR>), g2, dim3(kThreads), 0, a.stream, p2);
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR>), g2, dim3(kThreads), 0, a.stream, p2);
     return hipGetLastError();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if (a.drop.thr != 0) return a.causal ? go(T_{}, T_{}) : go(F_{}, T_{});
-  return a.causal ? go(T_{}, F_{}) : go(F_{}, F_{});
+  return a.drop.thr != 0 ? go(T_{}) : go(F_{});
 }
 
 }  // namespace
