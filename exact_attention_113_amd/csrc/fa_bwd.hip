@@ -82,29 +82,55 @@ __device__ __forceinline__ void load_rows64(const uint16_t* Xh, size_t stride, i
   }
 }
 
-// Row-wise operand: lane (i + 32 hi), k-step kk -> row r0 + i, dims 16 kk + 8 hi ..
+// Per-lane byte offsets of the operand reads inside a tile, for row bases
+// that are multiples of 16 (the swizzle repeats every 16 rows). They are
+// computed once per kernel and made opaque to the compiler, so that every
+// read is this register plus its tile's and rows' base as the instruction's
+// constant offset (without that, the compiler re-added tile bases per block
+// and spilled the partial sums).
+//   row[kk]   row-wise operand: lane (i + 32 hi), k-step kk -> row i,
+//             dims 16 kk + 8 hi ..
+//   tlo/tup   transposed operand: lane (j + 32 hi) -> column 32 db + j at
+//             rows {4hi + 0..3} (tlo) and {8 + 4hi + 0..3} (tup)
 template <int D>
-__device__ __forceinline__ u32x4 rd_row(const char* tile, int r0, int lq, int hi, int kk) {
-  constexpr int CH = D / 8, ROWB = 2 * D;
-  const int r = r0 + lq;
-  return *(const u32x4*)(tile + r * ROWB + 16 * ((2 * kk + hi) ^ swz<CH>(r)));
+struct LdsOffsets {
+  static constexpr int CH = D / 8, ROWB = 2 * D;
+  int row[D / 16];
+  int tlo[D / 32], tup[D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int lq = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      row[kk] = lq * ROWB + 16 * ((2 * kk + hi) ^ swz<CH>(lq));
+      asm volatile("" : "+v"(row[kk]));
+    }
+    const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1;
+    const int rlo = 4 * hi + tj, rup = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + 2 * dsub + (tm >> 1);
+      tlo[db] = rlo * ROWB + 16 * (c ^ swz<CH>(rlo)) + 8 * (tm & 1);
+      tup[db] = rup * ROWB + 16 * (c ^ swz<CH>(rup)) + 8 * (tm & 1);
+      asm volatile("" : "+v"(tlo[db]), "+v"(tup[db]));
+    }
+  }
+};
+
+// Row-wise operand of k-step kk from rows r0 .. r0 + 31 of a tile.
+template <int D>
+__device__ __forceinline__ u32x4 rd_row(const char* tile, int r0, const LdsOffsets<D>& lo, int kk) {
+  return *(const u32x4*)(tile + r0 * (2 * D) + lo.row[kk]);
 }
 
-// Transposed operand: lane (j + 32 hi) -> column 32 db + j at rows
-// {r0 + 4hi + 0..3, r0 + 8 + 4hi + 0..3} (r0 a multiple of 16).
+// Transposed operand of column block db from rows r0 .. r0 + 15 of a tile.
 template <int D>
-__device__ __forceinline__ u32x4 rd_tr(const char* tile, int r0, int lane, int db) {
-  constexpr int CH = D / 8, ROWB = 2 * D;
-  const int tj = (lane & 15) >> 2, tm = lane & 3, dsub = (lane >> 4) & 1, hi = lane >> 5;
-  const int c = 4 * db + 2 * dsub + (tm >> 1);
-  const int rlo = r0 + 4 * hi + tj, rup = rlo + 8;
-  const char* plo = tile + rlo * ROWB + 16 * (c ^ swz<CH>(rlo)) + 8 * (tm & 1);
-  const char* pup = tile + rup * ROWB + 16 * (c ^ swz<CH>(rup)) + 8 * (tm & 1);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)plo);
-  const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pup);
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-  const u32x2 u2 = __builtin_bit_cast(u32x2, up);
-  return u32x4{l2[0], l2[1], u2[0], u2[1]};
+__device__ __forceinline__ u32x4 rd_tr(const char* tile, int r0, const LdsOffsets<D>& lo, int db) {
+  const char* base = tile + r0 * (2 * D);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + lo.tlo[db]));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + lo.tup[db]));
+  const u32x2 a2 = __builtin_bit_cast(u32x2, a);
+  const u32x2 b2 = __builtin_bit_cast(u32x2, b);
+  return u32x4{a2[0], a2[1], b2[0], b2[1]};
 }
 
 // ---------------------------------------------------------------- delta, LSE
@@ -244,6 +270,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   const int N = sr0.N;
   const int k0 = kt * BK;
   if (k0 >= N) return;  // a key tile past the end of a shorter sequence
+  LdsOffsets<D> ldo;
+  ldo.init(lane);
 
   // This pair's 32 keys as the B operand of S = Q K^T (role A) or of
   // dP = dO V^T (role B): lane (key lq, half hi), k-step kk -> row[16kk + 8hi ..].
@@ -308,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(qt, 32 * qb, lq, hi, kk), bf[kk], s);
+    for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(qt, 32 * qb, ldo, kk), bf[kk], s);
     float p[16];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -356,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(gt, 32 * qb, lq, hi, kk), bf[kk], dp);
+    for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(gt, 32 * qb, ldo, kk), bf[kk], dp);
   };
 
   // Role A, phase 2: dV^T += dO^T P.
@@ -365,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc[db] = TT::mma(rd_tr<D>(gt, 32 * qb + 16 * h, lane, db), pp[h], acc[db]);
+        acc[db] = TT::mma(rd_tr<D>(gt, 32 * qb + 16 * h, ldo, db), pp[h], acc[db]);
   };
 
   // Role B, phase 2: dS = P (dP - delta), dK^T += Q^T dS.
@@ -401,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc[db] = TT::mma(rd_tr<D>(qt, 32 * qb + 16 * h, lane, db), sp[h], acc[db]);
+        acc[db] = TT::mma(rd_tr<D>(qt, 32 * qb + 16 * h, ldo, db), sp[h], acc[db]);
   };
 
   // One query tile of one role: phase 1, barrier (P visible), phase 2.
@@ -512,6 +540,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   const int N = sr.N;
   const int q0 = qt * BM;
   if (q0 >= N) return;  // a query tile past the end of a shorter sequence
+  LdsOffsets<D> ldo;
+  ldo.init(lane);
   const uint16_t* Kh = prm.k + sr.kvbase;
   const uint16_t* Vh = prm.v + sr.kvbase;
 
@@ -560,10 +590,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
     // The two products one after the other (fenced), so that at most one
     // set of operand fragments is live at a time.
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(kt, 32 * half, lq, hi, kk), qf[kk], s);
+    for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(kt, 32 * half, ldo, kk), qf[kk], s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(vt, 32 * half, lq, hi, kk), gf[kk], dp);
+    for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(vt, 32 * half, ldo, kk), gf[kk], dp);
     __builtin_amdgcn_sched_barrier(0);
     float ds[16];
     uint32_t kept = 0xffffu;
@@ -592,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc[db] = TT::mma(rd_tr<D>(kt, 32 * half + 16 * h, lane, db), sp[h], acc[db]);
+        acc[db] = TT::mma(rd_tr<D>(kt, 32 * half + 16 * h, ldo, db), sp[h], acc[db]);
   };
   auto any_block = [&] __device__ (int b, const char* kt, const char* vt) __attribute__((always_inline)) {
     if (b > last_b) return;
