@@ -268,6 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   const int hk = unit / prm.batch, bidx = unit - hk * prm.batch;
   const SeqRows sr0 = seq_rows<D>(prm, bidx, hk * prm.group, hk);
   const int N = sr0.N;
+  // Element and statistics offsets from one query head to the next (the
+  // group's heads are consecutive), so the loop below never re-reads the
+  // sequence offsets.
+  const size_t q_head = prm.cu ? (size_t)D : (size_t)N * D;
+  const size_t s_head = prm.cu ? (size_t)prm.total : (size_t)N;
   const int k0 = kt * BK;
   if (k0 >= N) return;  // a key tile past the end of a shorter sequence
   LdsOffsets<D> ldo;
@@ -312,14 +317,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   // tile's lse2 (0..63) and delta (64..127) values into a register, stored
   // to LDS by store_stats once this iteration's reads are done.
   auto load_qtile = [&] __device__ (int u, char* qd, char* gd) __attribute__((always_inline)) {
-    const int h = item_head(u), i = item_tile(u);
-    const SeqRows sr = seq_rows<D>(prm, bidx, h, hk);
-    load_rows64<D>(prm.q + sr.qbase, sr.qstride, i * BM, N, qd, w, lane);
-    load_rows64<D>(prm.dout + sr.qbase, sr.qstride, i * BM, N, gd, w, lane);
+    const int g = u / nqg, i = i_begin + (u - g * nqg);
+    const size_t qbase = sr0.qbase + (size_t)g * q_head, sbase = sr0.sbase + (size_t)g * s_head;
+    load_rows64<D>(prm.q + qbase, sr0.qstride, i * BM, N, qd, w, lane);
+    load_rows64<D>(prm.dout + qbase, sr0.qstride, i * BM, N, gd, w, lane);
     float v = 0.f;
     if (tid < 2 * BM) {
       const int row = min(i * BM + (tid & (BM - 1)), N - 1);
-      v = tid < BM ? prm.lse2[sr.sbase + row] : prm.delta[sr.sbase + row];
+      v = tid < BM ? prm.lse2[sbase + row] : prm.delta[sbase + row];
     }
     return v;
   };
