@@ -282,16 +282,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   // dP = dO V^T (role B): lane (key lq, half hi), k-step kk -> row[16kk + 8hi ..].
   const int kw0 = k0 + 32 * pair;
   const int key = kw0 + lq;
+  // All loads go out together: keys past N read key N - 1 and are zeroed
+  // afterwards (a load under a per-key branch made the compiler wait for the
+  // first ones before issuing the rest).
   u32x4 bf[KK];
   {
-    const uint16_t* Xh = (role_a ? prm.k : prm.v) + sr0.kvbase;
+    const uint16_t* Xh = (role_a ? prm.k : prm.v) + sr0.kvbase +
+                         (size_t)min(key, N - 1) * sr0.kvstride + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < N) x = *(const u32x4*)(Xh + (size_t)key * sr0.kvstride + 16 * kk + 8 * hi);
-      // K sign-flipped for negative scale: S = Q (-K)^T (exact).
-      bf[kk] = role_a ? (x ^ qsign) : x;
-    }
+    for (int kk = 0; kk < KK; ++kk) bf[kk] = *(const u32x4*)(Xh + 16 * kk);
+    const uint32_t kmask = key < N ? 0xffffffffu : 0u;
+    // K sign-flipped for negative scale: S = Q (-K)^T (exact).
+    const uint32_t ksign = role_a ? qsign : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) bf[kk] = (bf[kk] ^ ksign) & kmask;
   }
   f32x16 acc[DB];  // dV^T (role A) or dK^T (role B): lane = key, register = dim
 #pragma unroll

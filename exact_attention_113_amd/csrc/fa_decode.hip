@@ -146,15 +146,20 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecParams 
   // Keys visible to this row within the chunk: [k_lo, lim).
   const int lim = min(min(L, L - prm.s_q + tq + 1), k_hi);
 
+  // All loads go out together: lanes past the tile's rows read row 0 and are
+  // zeroed afterwards (a load under a per-row branch made the compiler wait
+  // for the first ones before issuing the rest).
   u32x4 qf[KK];
   {
-    const uint16_t* qrow = prm.q + ((size_t)(b * prm.s_q + tq) * prm.heads + h) * D;
+    const int lqc = row_ok ? lq : 0;
+    const int gqc = lqc / prm.s_q, tqc = lqc - gqc * prm.s_q;
+    const uint16_t* qrow =
+        prm.q + ((size_t)(b * prm.s_q + tqc) * prm.heads + hk * prm.group + gqc) * D + (D / 2) * hi;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *(const u32x4*)(qrow + (D / 2) * hi + 8 * kk);
-      qf[kk] = x ^ prm.qsign;
-    }
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const u32x4*)(qrow + 8 * kk);
+    const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = (qf[kk] ^ prm.qsign) & qmask;
   }
   wait_vm<0>(qf);
 

@@ -180,13 +180,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
   // lane (query lq, half hi), k-step kk -> Q[row][16*kk + 8*hi + 0..7].
   const int qw0 = q0 + 32 * w;
   const int qi = qw0 + lq;
+  // All eight loads go out together (rows past N read row N - 1 and are
+  // zeroed afterwards: a load under a per-row branch made the compiler wait
+  // for the first ones before issuing the rest).
   u32x4 qf[KK];
+  const uint16_t* qrow = Qh + (size_t)min(qi, N - 1) * sq + 8 * hi;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * sq + 16 * kk + 8 * hi);
-    qf[kk] = x ^ qsign;  // sign flip for negative scale (exact)
-  }
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const u32x4*)(qrow + 16 * kk);
+  const uint32_t qmask = qi < N ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = (qf[kk] ^ qsign) & qmask;  // sign flip for negative scale (exact)
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -487,18 +490,40 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
   // O = acc / sum rounded to the dtype; LSE = ln 2 * (ref + log2 sum).
   const float ltot = half_swap_sum(lsum);
   const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
-  if (qi < N) {
-    uint16_t* orow = prm.o + qbase + (size_t)qi * sq;
+  if (qi < N && hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
+  // O leaves through LDS so that every global store writes whole rows:
+  // a lane holds 4 consecutive head-dim values of one row per register
+  // group, so direct stores would write 16 bytes per row per instruction.
+  // Each wave stages its 32 x D tile (rows at ROWB bytes, 16-byte chunks
+  // XOR-swizzled by row) in half of one tile buffer, free once every wave
+  // has finished its last P V product.
+  __syncthreads();
+  char* stage;
+  {
+    const int bsel = w >> 1;
+    char* buf = bsel == 0 ? kb0 : bsel == 1 ? kb1 : bsel == 2 ? vb0 : vb1;
+    stage = buf + (w & 1) * 32 * ROWB;
+  }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 out;
-        out[0] = TT::pack2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
-        out[1] = TT::pack2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-        *(u32x2*)(orow + 32 * db + 8 * g4 + 4 * hi) = out;
-      }
-    if (hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2 out;
+      out[0] = TT::pack2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
+      out[1] = TT::pack2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+      const int chunk = (4 * db + g4) ^ (lq % CH);
+      *(u32x2*)(stage + lq * ROWB + 16 * chunk + 8 * hi) = out;
+    }
+  // Read back row-wise (CH lanes per row, 64 / CH rows per instruction) and
+  // store 16 bytes per lane; the wave reads only what it wrote.
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  constexpr int RPS = 64 / CH;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPS; ++i) {
+    const int r = i * RPS + lane / CH, cpos = lane % CH;
+    const u32x4 val = *(const u32x4*)(stage + r * ROWB + 16 * (cpos ^ (r % CH)));
+    const int row = qw0 + r;
+    if (row < N) *(u32x4*)(prm.o + qbase + (size_t)row * sq + 8 * cpos) = val;
   }
 }
 
