@@ -500,18 +500,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 
   // dK = scale * acc (role B), dV = acc (role A), rounded to the dtype. Lane
   // lq holds key kw0 + lq; register r holds dim 32 db + 8(r/4) + 4 hi + r%4.
-  if (key < N) {
-    uint16_t* out = (role_a ? prm.dv : prm.dk) + sr0.kvbase + (size_t)key * sr0.kvstride;
+  // The rows leave through LDS (store_tile_rows), each wave's tile in half of
+  // one query tile buffer once every wave is done with them.
+  __syncthreads();
+  {
+    const int bsel = w >> 1;
+    char* buf = bsel == 0 ? qt0 : bsel == 1 ? qt1 : bsel == 2 ? gt0 : gt1;
     const float sc = role_a ? (DROP ? drop.inv_keep : 1.f) : prm.grad_scale;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 o;
-        o[0] = TT::pack2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc);
-        o[1] = TT::pack2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc);
-        *(u32x2*)(out + 32 * db + 8 * g4 + 4 * hi) = o;
-      }
+    store_tile_rows<TT, D>(acc, sc, buf + (w & 1) * 32 * (2 * D),
+                           (role_a ? prm.dv : prm.dk) + sr0.kvbase + (size_t)kw0 * sr0.kvstride,
+                           sr0.kvstride, N - kw0, lane);
   }
 }
 
@@ -664,18 +662,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   }
 
   // dQ = scale * acc, rounded to the dtype: lane lq holds query qi; register
-  // r holds dim 32 db + 8(r/4) + 4 hi + r%4.
-  if (qi < N) {
-    uint16_t* out = prm.dq + sr.qbase + (size_t)qi * sr.qstride;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 o;
-        o[0] = TT::pack2(acc[db][4 * g4] * dq_scale, acc[db][4 * g4 + 1] * dq_scale);
-        o[1] = TT::pack2(acc[db][4 * g4 + 2] * dq_scale, acc[db][4 * g4 + 3] * dq_scale);
-        *(u32x2*)(out + 32 * db + 8 * g4 + 4 * hi) = o;
-      }
+  // r holds dim 32 db + 8(r/4) + 4 hi + r%4. The rows leave through LDS
+  // (store_tile_rows), each wave's tile in half of one K/V tile buffer once
+  // every wave is done with them.
+  __syncthreads();
+  {
+    const int bsel = w >> 1;
+    char* buf = bsel == 0 ? kb0 : bsel == 1 ? kb1 : bsel == 2 ? vb0 : vb1;
+    store_tile_rows<TT, D>(acc, dq_scale, buf + (w & 1) * 32 * (2 * D),
+                           prm.dq + sr.qbase + (size_t)qw0 * sr.qstride, sr.qstride, N - qw0,
+                           lane);
   }
 }
 

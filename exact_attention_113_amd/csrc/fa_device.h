@@ -92,6 +92,43 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Store one wave's 32 x D tile of fp32 MFMA results (lane (row lq, half hi),
+// block db, register r -> column 32 db + 8 (r / 4) + 4 hi + r % 4), times the
+// lane's factor sc and rounded to TT, as whole rows. Straight from that
+// layout a store instruction would write 16 bytes into each of 32 rows; the
+// tile goes through `stage` instead (32 * 2D bytes of LDS that only this wave
+// uses, 16-byte chunks XOR-swizzled by row so that both the writes and the
+// row-wise reads spread over the banks) and each lane then stores 16
+// contiguous bytes, D / 8 lanes per row. Row r goes to out + r * stride
+// (elements) when r < nrows.
+template <typename TT, int D>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], float sc, char* stage,
+                                                uint16_t* out, size_t stride, int nrows,
+                                                int lane) {
+  constexpr int CH = D / 8;     // 16-byte chunks per row
+  constexpr int ROWB = 2 * D;   // bytes per row
+  constexpr int RPS = 64 / CH;  // rows per store instruction
+  const int lq = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2 v;
+      v[0] = TT::pack2(acc[db][4 * g4 + 0] * sc, acc[db][4 * g4 + 1] * sc);
+      v[1] = TT::pack2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc);
+      const int chunk = (4 * db + g4) ^ (lq % CH);
+      *(u32x2*)(stage + lq * ROWB + 16 * chunk + 8 * hi) = v;
+    }
+  // LDS operations of one wave complete in order: the reads below see the
+  // writes above.
+#pragma unroll
+  for (int i = 0; i < 32 / RPS; ++i) {
+    const int r = i * RPS + lane / CH, cpos = lane % CH;
+    const u32x4 v = *(const u32x4*)(stage + r * ROWB + 16 * (cpos ^ (r % CH)));
+    if (r < nrows) *(u32x4*)(out + (size_t)r * stride + 8 * cpos) = v;
+  }
+}
+
 // ---- dropout bits -----------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): ten rounds on a 128-bit counter with a 64-bit

@@ -491,12 +491,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
   const float ltot = half_swap_sum(lsum);
   const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
   if (qi < N && hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
-  // O leaves through LDS so that every global store writes whole rows:
-  // a lane holds 4 consecutive head-dim values of one row per register
-  // group, so direct stores would write 16 bytes per row per instruction.
-  // Each wave stages its 32 x D tile (rows at ROWB bytes, 16-byte chunks
-  // XOR-swizzled by row) in half of one tile buffer, free once every wave
-  // has finished its last P V product.
+  // O leaves through LDS as whole rows (store_tile_rows), each wave's tile
+  // in half of one tile buffer, free once every wave has finished its last
+  // P V product.
   __syncthreads();
   char* stage;
   {
@@ -504,27 +501,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
     char* buf = bsel == 0 ? kb0 : bsel == 1 ? kb1 : bsel == 2 ? vb0 : vb1;
     stage = buf + (w & 1) * 32 * ROWB;
   }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      u32x2 out;
-      out[0] = TT::pack2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
-      out[1] = TT::pack2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-      const int chunk = (4 * db + g4) ^ (lq % CH);
-      *(u32x2*)(stage + lq * ROWB + 16 * chunk + 8 * hi) = out;
-    }
-  // Read back row-wise (CH lanes per row, 64 / CH rows per instruction) and
-  // store 16 bytes per lane; the wave reads only what it wrote.
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  constexpr int RPS = 64 / CH;  // rows per store instruction
-#pragma unroll
-  for (int i = 0; i < 32 / RPS; ++i) {
-    const int r = i * RPS + lane / CH, cpos = lane % CH;
-    const u32x4 val = *(const u32x4*)(stage + r * ROWB + 16 * (cpos ^ (r % CH)));
-    const int row = qw0 + r;
-    if (row < N) *(u32x4*)(prm.o + qbase + (size_t)row * sq + 8 * cpos) = val;
-  }
+  store_tile_rows<TT, D>(oacc, inv, stage, prm.o + qbase + (size_t)qw0 * sq, sq, N - qw0, lane);
 }
 
 template <typename TT, int D>
