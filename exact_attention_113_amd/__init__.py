@@ -174,9 +174,9 @@ def backward_workspace_bytes(B, H, N, D):
 
 
 def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, dropout_p=0.0,
-             seed=0, offset=0):
+             seed=0, offset=0, out=None):
     """Backward from the forward's o and lse (and its dropout arguments).
-    Returns (dq, dk, dv)."""
+    Returns (dq, dk, dv); `out` may give the three output tensors."""
     _check_qkv(q, k, v)
     for name, t in (("o", o), ("do", do)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
@@ -189,7 +189,14 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, drop
     need = backward_workspace_bytes(B, H, N, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or \
+                    not t.is_contiguous():
+                raise ValueError(f"{name} must match q (shape, dtype, device, contiguous)")
     lib = _lib.load()
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),

@@ -14,8 +14,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def packed(lengths, H, H_kv, D, dtype, seed):
-    total = sum(lengths)
+def packed(lengths, H, H_kv, D, dtype, seed, extra=0):
+    total = sum(lengths) + extra
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     td = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
@@ -98,3 +98,22 @@ def test_prefill_batch_workload_sampled():
         assert_close(f"seq {b} head {h} O", to64(o[s0:s1, h])[None, None], ro, "bf16",
                      strict=True)
         assert_lse_close(f"seq {b} head {h}", to64(lse[h, s0:s1])[None, None], rl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_uncovered_rows_untouched(D):
+    """Tokens after the last sequence keep the caller's O and LSE; the rows of
+    each sequence are written up to its end and no further (a sequence of 200
+    tokens ends inside a 256-row tile, the next starts right after it)."""
+    lengths = [200, 33, 300]
+    q, k, v, cu = packed(lengths, 4, 2, D, "bf16", seed=733 + D, extra=70)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((4, q.shape[0]), 7.0, dtype=torch.float32, device=DEV)
+    fa.forward_varlen(q, k, v, cu_t, max(lengths), causal=True, scale=0.1, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_forward_varlen(to64(q), to64(k), to64(v), cu, 0.1, True)
+    n = cu[-1]
+    assert_close("covered O", to64(o)[:n], ro[:n], "bf16")
+    assert_lse_close("covered", to64(lse)[:, :n], rl[:, :n])
+    assert bool((o[n:] == 7).all()) and bool((lse[:, n:] == 7).all())
