@@ -1,6 +1,6 @@
 // Fused attention forward for bf16/fp16 inputs on gfx950.
 //
-// One workgroup owns BM = 256 (or 128) query rows of one (batch, head) and streams
+// One workgroup owns 256 (or 128) query rows of one (batch, head) and streams
 // the key/value rows through LDS, keeping per query row a running maximum,
 // a running sum of exponentials and an unnormalised fp32 output accumulator
 // (online softmax: "From Self-Attention to FlashAttention", section 2;
@@ -9,8 +9,9 @@
 // logsumexp are the only results written back (the flash data flow of
 // section 1 of the first page: only O goes back to HBM).
 //
-// Waves. Eight waves, two per SIMD (four for short sequences, two
-// workgroups per CU), each owning 32 consecutive query rows.
+// Waves. Eight waves, two per SIMD, each owning 32 consecutive query rows
+// and all of their keys; for short sequences, two waves per 32 rows, each
+// taking every other 32-key block, merged at the end.
 // Scores are computed transposed, S^T = K Q^T (32x32x16 MFMA, fp32
 // accumulate): lane j and j + 32 share one query and each holds 16 of a
 // 32-key block's scores, so row maxima and sums are in-register reductions
@@ -46,16 +47,17 @@
 namespace fa {
 namespace {
 
-// Waves per workgroup (NW, 32 query rows each): 8 (two per SIMD, one
-// workgroup per CU) when that gives at least kMinGrid workgroups, else 4
-// (128 rows, two workgroups per CU) so that short sequences spread over
-// more CUs. Each wave runs the same code in both cases, so the results are
-// identical. (Two waves of 64 rows measured slower than four: with 64 KiB
-// of LDS per workgroup they leave one wave per SIMD.)
+// Workgroups of eight waves, one per CU. Each wave takes 32 rows and all of
+// their keys (256 rows per workgroup) when that gives at least kMinGrid
+// workgroups. Otherwise (short sequences) a workgroup takes 128 rows and the
+// two waves of each 32-row group split the keys (KS = 2): the key loop, the
+// critical path of such short grids, halves, and a SIMD still runs two
+// waves. (Four-wave workgroups of 128 rows with whole key ranges, one wave
+// per SIMD, measured 8 % slower at N = 1024 and 15 % at B2 H8 N512 D64.)
 #ifndef FA_FWD_MIN_GRID
 #define FA_FWD_MIN_GRID 512
 #endif
-constexpr int64_t kMinGrid = FA_FWD_MIN_GRID;  // workgroups wanted before shrinking them
+constexpr int64_t kMinGrid = FA_FWD_MIN_GRID;  // workgroups wanted before splitting keys
 constexpr int kBN = 64;                 // keys per LDS tile
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
@@ -121,9 +123,14 @@ struct FwdParams {
 // the keys to mask. (A separate full-attention instantiation, with its mask
 // folded away at compile time, came out of register allocation with spills
 // in the key loop and ran 1.46x slower at N = 4096, D = 128.)
-template <typename TT, int D, int NW, bool DROP>
-__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const FwdParams prm) {
-  constexpr int kBM = 32 * NW;                // query rows per workgroup
+template <typename TT, int D, int NW, bool DROP, int KS>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
+  // KS = 2 (short sequences): the waves form NW / 2 row groups of 32 rows,
+  // and the two waves of a group take alternate 32-key blocks of its keys,
+  // halving the key loop's length; their partial results are merged at the
+  // end (the same rescale-and-add as between blocks of the online softmax).
+  constexpr int NRG = NW / KS;                // row groups of 32 query rows
+  constexpr int kBM = 32 * NRG;               // query rows per workgroup
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                 // bytes per row
   constexpr int TILEB = kBN * ROWB;           // bytes per K or V tile
@@ -136,10 +143,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
   __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
   __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
+  __shared__ float xm[KS == 2 ? NRG : 1][64], xl[KS == 2 ? NRG : 1][64];  // merge of key halves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 31, hi = lane >> 5;
+  const int rg = w % NRG, kh = w / NRG;  // row group; key half (KS = 2)
 
   const float c = prm.c;
   const uint32_t qsign = prm.qsign;
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
 
   // This wave's 32 query rows and their B operands of S^T = K Q^T:
   // lane (query lq, half hi), k-step kk -> Q[row][16*kk + 8*hi + 0..7].
-  const int qw0 = q0 + 32 * w;
+  const int qw0 = q0 + 32 * rg;
   const int qi = qw0 + lq;
   // All eight loads go out together (rows past N read row N - 1 and are
   // zeroed afterwards: a load under a per-row branch made the compiler wait
@@ -411,8 +420,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
                   f32x16& nxt, const u32x4 (&pprev)[2], u32x4 (&pcur)[2])
       __attribute__((always_inline)) {
     apply_rescale();
-    scores(kt, (b + 1) & 1, nxt);
-    if constexpr (decltype(has_pv)::value) pv(vt, (b - 1) & 1, pprev);
+    scores(kt, KS == 1 ? (b + 1) & 1 : kh, nxt);
+    if constexpr (decltype(has_pv)::value) pv(vt, KS == 1 ? (b - 1) & 1 : kh, pprev);
     softmax(edge, b, cur, pcur);
   };
   // A step of a wave whose rows may need masks or be done: the full step
@@ -450,58 +459,145 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_kernel(const Fwd
     if (T + 1 < ntile) load_tile(Vh, T + 1, vdst, true);
   };
 
-  // Prologue: K tiles 0 and 1 and V tile 0, then the scores of block 0 and
-  // step 0 (no P V yet).
+  // Prologue: K tiles 0 and 1 and V tile 0.
   load_tile(Kh, 0, kb0, false);
   load_tile(Vh, 0, vb0, true);
   if (ntile > 1) load_tile(Kh, 1, kb1, false);
   wait_vmem();
   __syncthreads();
-  if (last_b >= 0) {
-    scores(kb0, 0, sA);
-    // Edge variant even without masks: the reference is not set yet, so
-    // step 0 takes the full softmax (with masks only where needed).
-    if (first_edge == 0) step(True{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
-    else step(Unmasked{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
-  }
 
-  // Two tiles per iteration so that every buffer is named statically:
-  // even tiles T read K from kb1 and V from vb0, odd tiles K from kb0 and
-  // V from vb1.
-  for (int T = 0; 2 * T + 1 < nb; T += 2) {
-    tile_barrier(T, kb0, vb1);
-    tile_steps(T, kb1, vb0);
-    if (2 * T + 3 < nb) {
-      tile_barrier(T + 1, kb1, vb0);
-      tile_steps(T + 1, kb0, vb1);
+  if constexpr (KS == 1) {
+    // The scores of block 0 and step 0 (no P V yet).
+    if (last_b >= 0) {
+      scores(kb0, 0, sA);
+      // Edge variant even without masks: the reference is not set yet, so
+      // step 0 takes the full softmax (with masks only where needed).
+      if (first_edge == 0) step(True{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
+      else step(Unmasked{}, False{}, 0, kb0, vb0, sA, sB, pB, pA);
+    }
+
+    // Two tiles per iteration so that every buffer is named statically:
+    // even tiles T read K from kb1 and V from vb0, odd tiles K from kb0 and
+    // V from vb1.
+    for (int T = 0; 2 * T + 1 < nb; T += 2) {
+      tile_barrier(T, kb0, vb1);
+      tile_steps(T, kb1, vb0);
+      if (2 * T + 3 < nb) {
+        tile_barrier(T + 1, kb1, vb0);
+        tile_steps(T + 1, kb0, vb1);
+      }
+    }
+    // The last step's P V when it was the workgroup's last step (its V tile
+    // becomes visible at this barrier).
+    wait_vmem();
+    __syncthreads();
+    if (last_b == nb - 1 && last_b >= 0) {
+      apply_rescale();
+      const u32x4(&pl)[2] = (last_b & 1) ? pB : pA;
+      if ((last_b >> 1) & 1) pv(vb1, last_b & 1, pl);
+      else pv(vb0, last_b & 1, pl);
+    }
+
+    // O = acc / sum rounded to the dtype; LSE = ln 2 * (ref + log2 sum).
+    const float ltot = half_swap_sum(lsum);
+    const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
+    if (qi < N && hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
+    // O leaves through LDS as whole rows (store_tile_rows), each wave's tile
+    // in half of one tile buffer, free once every wave has finished its last
+    // P V product.
+    __syncthreads();
+    char* stage;
+    {
+      const int bsel = w >> 1;
+      char* buf = bsel == 0 ? kb0 : bsel == 1 ? kb1 : bsel == 2 ? vb0 : vb1;
+      stage = buf + (w & 1) * 32 * ROWB;
+    }
+    store_tile_rows<TT, D>(oacc, inv, stage, prm.o + qbase + (size_t)qw0 * sq, sq, N - qw0, lane);
+  } else {
+    // Key halves: this wave's step j computes block 2j + kh, the kh half of
+    // K/V tile j, so one step per tile. K tile t lives in kb[t % 2] and V
+    // tile t in vb[t % 2]; step j reads K tile j + 1 and V tile j - 1, and
+    // the barrier before it sends K tile j + 2 and V tile j into the
+    // buffers step j - 1 was the last to read. K tile 2 goes out once every
+    // wave has taken block kh's scores from K tile 0.
+    const int jl = last_b >= kh ? (last_b - kh) / 2 : -1;  // this wave's last step
+    const int jmax = (nb - 1) / 2;                         // the workgroup's last block step
+    if (jl >= 0) scores(kb0, kh, sA);
+    __syncthreads();
+    if (ntile > 2) load_tile(Kh, 2, kb0, false);
+    if (jl >= 0) {
+      if (first_edge <= kh) step(True{}, False{}, kh, kb1, vb0, sA, sB, pB, pA);
+      else step(Unmasked{}, False{}, kh, kb1, vb0, sA, sB, pB, pA);
+    }
+    auto half_step = [&](int j, const char* kt, const char* vt, f32x16& cur, f32x16& nxt,
+                         const u32x4(&pprev)[2], u32x4(&pcur)[2]) __attribute__((always_inline)) {
+      const int b = 2 * j + kh;
+      if (j <= jl) {
+        if (b >= first_edge) step(True{}, True{}, b, kt, vt, cur, nxt, pprev, pcur);
+        else step(False{}, True{}, b, kt, vt, cur, nxt, pprev, pcur);
+      } else if (j == jl + 1) {
+        apply_rescale();
+        pv(vt, kh, pprev);
+      }
+    };
+    for (int j = 1; j <= jmax + 1; j += 2) {
+      wait_vmem();
+      __syncthreads();
+      if (j + 2 < ntile) load_tile(Kh, j + 2, kb1, false);
+      if (j < ntile) load_tile(Vh, j, vb1, true);
+      half_step(j, kb0, vb0, sB, sA, pA, pB);
+      if (j + 1 <= jmax + 1) {
+        wait_vmem();
+        __syncthreads();
+        if (j + 3 < ntile) load_tile(Kh, j + 3, kb0, false);
+        if (j + 1 < ntile) load_tile(Vh, j + 1, vb0, true);
+        half_step(j + 1, kb1, vb1, sA, sB, pB, pA);
+      }
+    }
+
+    // The wave of key half 1 hands its reference maximum, sum share and
+    // accumulator to the wave of half 0 with the same rows, through the tile
+    // buffer of its row group (free once every wave is past its last P V);
+    // that wave rescales both to the larger reference, adds, and stores.
+    wait_vmem();
+    __syncthreads();
+    float* xo = (float*)(rg == 0 ? kb0 : rg == 1 ? kb1 : rg == 2 ? vb0 : vb1);
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(xo + 4 * ((db * 4 + r4) * 64 + lane)) =
+              f32x4{oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2],
+                    oacc[db][4 * r4 + 3]};
+      xm[rg][lane] = mref;
+      xl[rg][lane] = lsum;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = xm[rg][lane], l1 = xl[rg][lane];
+      const float mm = fmaxf(mref, m1);
+      const float a0 = mref == -INFINITY ? 0.f : fast_exp2(mref - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+      lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 o1 = *(const f32x4*)(xo + 4 * ((db * 4 + r4) * 64 + lane));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[db][4 * r4 + e] = oacc[db][4 * r4 + e] * a0 + o1[e] * a1;
+        }
+      mref = mm;
+      const float ltot = half_swap_sum(lsum);
+      const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
+      if (qi < N && hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
+      // The wave has read all of its row group's buffer: it stages its rows
+      // there (store_tile_rows).
+      store_tile_rows<TT, D>(oacc, inv, (char*)xo, prm.o + qbase + (size_t)qw0 * sq, sq,
+                             N - qw0, lane);
     }
   }
-  // The last step's P V when it was the workgroup's last step (its V tile
-  // becomes visible at this barrier).
-  wait_vmem();
-  __syncthreads();
-  if (last_b == nb - 1 && last_b >= 0) {
-    apply_rescale();
-    const u32x4(&pl)[2] = (last_b & 1) ? pB : pA;
-    if ((last_b >> 1) & 1) pv(vb1, last_b & 1, pl);
-    else pv(vb0, last_b & 1, pl);
-  }
-
-  // O = acc / sum rounded to the dtype; LSE = ln 2 * (ref + log2 sum).
-  const float ltot = half_swap_sum(lsum);
-  const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
-  if (qi < N && hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
-  // O leaves through LDS as whole rows (store_tile_rows), each wave's tile
-  // in half of one tile buffer, free once every wave has finished its last
-  // P V product.
-  __syncthreads();
-  char* stage;
-  {
-    const int bsel = w >> 1;
-    char* buf = bsel == 0 ? kb0 : bsel == 1 ? kb1 : bsel == 2 ? vb0 : vb1;
-    stage = buf + (w & 1) * 32 * ROWB;
-  }
-  store_tile_rows<TT, D>(oacc, inv, stage, prm.o + qbase + (size_t)qw0 * sq, sq, N - qw0, lane);
 }
 
 template <typename TT, int D>
@@ -522,18 +618,19 @@ hipError_t launch_half(const FwdArgs& a) {
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
   p.drop = a.drop;
   p.diag = a.causal ? 0 : (int)a.N;
-  auto go = [&](auto nw) {
-    constexpr int NW = decltype(nw)::value;
-    p.n_qtiles = (int)((a.N + 32 * NW - 1) / (32 * NW));
+  auto go = [&](auto ks) {
+    constexpr int KS = decltype(ks)::value;
+    constexpr int BM = 256 / KS;
+    p.n_qtiles = (int)((a.N + BM - 1) / BM);
     const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.bh_count));
     if (a.drop.thr != 0)
-      hipLaunchKernelGGL((fwd_kernel<TT, D, NW, true>), grid, dim3(64 * NW), 0, a.stream, p);
+      hipLaunchKernelGGL((fwd_kernel<TT, D, 8, true, KS>), grid, dim3(512), 0, a.stream, p);
     else
-      hipLaunchKernelGGL((fwd_kernel<TT, D, NW, false>), grid, dim3(64 * NW), 0, a.stream, p);
+      hipLaunchKernelGGL((fwd_kernel<TT, D, 8, false, KS>), grid, dim3(512), 0, a.stream, p);
   };
   const int64_t bh = a.B * a.H;
-  if (((a.N + 255) / 256) * bh >= kMinGrid) go(std::integral_constant<int, 8>{});
-  else go(std::integral_constant<int, 4>{});
+  if (((a.N + 255) / 256) * bh >= kMinGrid) go(std::integral_constant<int, 1>{});
+  else go(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 
