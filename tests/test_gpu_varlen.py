@@ -117,3 +117,14 @@ def test_uncovered_rows_untouched(D):
     assert_close("covered O", to64(o)[:n], ro[:n], "bf16")
     assert_lse_close("covered", to64(lse)[:, :n], rl[:, :n])
     assert bool((o[n:] == 7).all()) and bool((lse[:, n:] == 7).all())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_packed_sequences_short_grid(D, causal):
+    """A few long sequences (so few 256-row tiles that the forward splits each
+    row group's keys between two waves) with grouped heads, every head against
+    the oracle: tiles end inside a sequence and the next one starts mid-tile."""
+    lengths = [700, 1333, 1, 517]
+    q, k, v, cu = packed(lengths, 4, 2, D, "bf16", seed=900 + D + int(causal))
+    run_and_check(f"long packed D{D} causal={causal}", q, k, v, cu, causal, D ** -0.5, "bf16")
