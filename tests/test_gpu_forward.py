@@ -187,3 +187,16 @@ def test_offsets_beyond_2g_elements():
     for tag, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv),
                            oracle_backward(q, k, v, do, D ** -0.5, True, heads)):
         assert_close(tag, pick(got, heads), r, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(4, 16, 2048), (8, 16, 1000)])
+def test_large_grid_d64(causal, shape):
+    """D = 64 on grids of at least 512 256-row tiles, the path that keeps four
+    K and four V tiles and synchronises once per two tiles (one shape with a
+    ragged last tile): sampled heads against the oracle."""
+    B, H, N = shape
+    q, k, v = workloads.make_random((B, H, N, 64), seed=3100 + N + int(causal), dtype="bf16",
+                                    device=DEV)
+    check(f"D64 B{B} H{H} N{N} causal={causal}", q, k, v, causal, 0.125, "bf16",
+          [(0, 0), (B // 2, 7), (B - 1, H - 1)])
