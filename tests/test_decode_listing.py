@@ -7,8 +7,8 @@ the compiled code leaves a load's destination registers alone until the wait
 that covers it. This test compiles fa_decode.hip to gfx950 assembly with the
 library's own flags and checks exactly that for every kernel instantiation:
 between an untracked load and the next wait of its kind, no instruction may
-read or write the registers it loads (the key loop is followed around its
-back edge).
+read or write the registers it loads, on any control-flow path (branches
+are followed both ways, the key loop around its back edge).
 """
 
 import os
@@ -43,15 +43,30 @@ def _dest(line):
     return set(range(int(m.group(1)), int(m.group(2)) + 1)) if m else set()
 
 
+def _successors(body, labels, k):
+    """Indices of the instructions that can run after body[k]."""
+    line = body[k]
+    op = line.split()[0]
+    if op == "s_endpgm":
+        return []
+    target = None
+    m = re.search(r"(\.LBB\w+)", line)
+    if op.startswith("s_branch") or op.startswith("s_cbranch"):
+        if m and m.group(1) in labels:
+            target = labels[m.group(1)]
+    if op.startswith("s_branch"):
+        return [target] if target is not None else []
+    nxt = [k + 1] if k + 1 < len(body) else []
+    return nxt + ([target] if target is not None else [])
+
+
 def violations(body):
-    """(load, offending instruction) pairs for one kernel's instruction list."""
-    heads = [k for k, l in enumerate(body) if "Loop Header" in l]
-    loop = None
-    if heads:
-        start = heads[0]
-        ends = [k for k, l in enumerate(body)
-                if k > start and l.startswith("s_cbranch") and ".LBB" in l]
-        loop = (start, max(ends))
+    """(load, offending instruction) pairs for one kernel's instruction list:
+    every path from an untracked load (following unconditional and both ways
+    of conditional branches, loops included) is walked up to the first wait
+    of its kind, and any instruction on it that reads or writes the load's
+    registers is reported."""
+    labels = {l[:-1]: k for k, l in enumerate(body) if l.endswith(":")}
     bad = []
     for k, line in enumerate(body):
         op = line.split()[0]
@@ -60,24 +75,25 @@ def violations(body):
         dst = _dest(line)
         assert dst, line
         kind = "vmcnt" if op.startswith("global") else "lgkmcnt(0)"
-        seq = body[k + 1:]
-        if loop and loop[0] <= k <= loop[1]:
-            seq = body[k + 1:loop[1] + 1] + body[loop[0]:k]
-        for t in seq:
+        seen = set()
+        stack = _successors(body, labels, k)
+        while stack:
+            i = stack.pop()
+            if i in seen:
+                continue
+            seen.add(i)
+            t = body[i]
             top = t.split()[0]
             if top == "s_waitcnt" and kind in t:
-                break
-            if top.endswith(":"):
                 continue
-            if top in ASYNC:
-                if _dest(t) & dst:
+            if not top.endswith(":"):
+                if top in ASYNC:
+                    rest = t.split(",", 1)[1] if "," in t else ""
+                    if (_dest(t) & dst) or (_regs(rest) & dst):
+                        bad.append((line, t))
+                elif _regs(t) & dst:
                     bad.append((line, t))
-                rest = t.split(",", 1)[1] if "," in t else ""
-                if _regs(rest) & dst:
-                    bad.append((line, t))
-                continue
-            if _regs(t) & dst:
-                bad.append((line, t))
+            stack.extend(_successors(body, labels, i))
     return bad
 
 
@@ -111,3 +127,25 @@ def test_checker_catches_a_planted_use():
             "v_add_f32_e32 v10, v4, v9"]
     assert len(violations(body)) == 1
     assert violations(body[:1] + body[2:]) == []
+
+
+def test_checker_follows_branches():
+    """A write in a block the load's path branches over is not a use; one in a
+    block a conditional branch can reach is."""
+    skipped = ["global_load_dwordx4 v[4:7], v[0:1], off",
+               "s_branch .LBB0_3",
+               ".LBB0_2:",
+               "v_mov_b32_e32 v4, 0",
+               ".LBB0_3:",
+               "s_waitcnt vmcnt(0)",
+               "v_add_f32_e32 v10, v4, v9",
+               "s_endpgm"]
+    assert violations(skipped) == []
+    reached = ["global_load_dwordx4 v[4:7], v[0:1], off",
+               "s_cbranch_scc1 .LBB0_2",
+               "s_waitcnt vmcnt(0)",
+               "s_endpgm",
+               ".LBB0_2:",
+               "v_mov_b32_e32 v5, 0",
+               "s_endpgm"]
+    assert len(violations(reached)) == 1
