@@ -115,3 +115,22 @@ def test_training_shape_sampled_head():
                                            2024, 7, bh0=bh0)
     for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), grads):
         assert_close(f"train dropout {name}", sl(g), r, "bf16", strict=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_dropout_large_grid_d64(causal):
+    """D = 64 with dropout on a grid of 512 256-row tiles (the forward path that
+    keeps four K and four V tiles and synchronises once per two tiles), with a
+    ragged last tile: two heads against the oracle, whose bits are keyed by
+    each head's own (batch, head) index."""
+    B, H, N, D = 8, 16, 1000, 64
+    q, k, v = rand((B, H, N, D), 4242 + int(causal))
+    kw = dict(causal=causal, scale=0.125, dropout_p=0.2, seed=77, offset=3)
+    o, lse = fa.forward(q, k, v, **kw)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (B - 1, H - 3)]:
+        sl = lambda t: to64(t[b:b + 1, h:h + 1])
+        ro, rl = orc.attention_forward_dropout(sl(q), sl(k), sl(v), 0.125, causal, 0.2, 77, 3,
+                                               bh0=b * H + h)
+        assert_close(f"dropout D64 large grid causal={causal} ({b},{h})", sl(o), ro, "bf16")
+        assert_lse_close("dropout D64 large grid", sl(lse), rl)
