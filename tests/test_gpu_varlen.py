@@ -128,3 +128,24 @@ def test_long_packed_sequences_short_grid(D, causal):
     lengths = [700, 1333, 1, 517]
     q, k, v, cu = packed(lengths, 4, 2, D, "bf16", seed=900 + D + int(causal))
     run_and_check(f"long packed D{D} causal={causal}", q, k, v, cu, causal, D ** -0.5, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_large_grid_d64(causal):
+    """A packed batch big enough for the whole-key-range D = 64 path (four K and
+    four V tiles, one barrier per two tiles): 16 sequences of 900..2100 tokens,
+    32 query over 8 K/V heads; sampled sequences and heads against the oracle."""
+    g = np.random.default_rng(2048 + int(causal))
+    lengths = [int(x) for x in g.integers(900, 2101, size=16)]
+    q, k, v, cu = packed(lengths, 32, 8, 64, "bf16", seed=2049 + int(causal))
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    o, lse = fa.forward_varlen(q, k, v, cu_t, max(lengths), causal=causal, scale=0.125)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (7, 19), (15, 31)]:
+        s0, s1 = cu[b], cu[b + 1]
+        hk = h // 4
+        ro, rl = orc.attention_forward(to64(q[s0:s1, h])[None, None],
+                                       to64(k[s0:s1, hk])[None, None],
+                                       to64(v[s0:s1, hk])[None, None], 0.125, causal)
+        assert_close(f"packed D64 seq {b} head {h}", to64(o[s0:s1, h])[None, None], ro, "bf16")
+        assert_lse_close(f"packed D64 seq {b} head {h}", to64(lse[h, s0:s1])[None, None], rl)
