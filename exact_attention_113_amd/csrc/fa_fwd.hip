@@ -31,10 +31,11 @@
 //
 // Memory path. K and V tiles of 64 keys go from global memory straight
 // into LDS with global_load_lds_dwordx4 (no staging registers), double
-// buffered, one barrier per tile. The four tile buffers are separate LDS
-// arrays addressed statically (the tile loop is unrolled by two), so the
-// compiler can tell that the operand reads of one buffer do not wait for
-// the direct loads still landing in another. Each 16-byte chunk of a row is
+// buffered, one barrier per tile (at D = 64: four buffers per tensor, one
+// barrier per two tiles). The tile buffers are separate LDS arrays
+// addressed statically (the tile loop is unrolled), so the compiler can
+// tell that the operand reads of one buffer do not wait for the direct
+// loads still landing in another. O leaves through LDS as whole rows. Each 16-byte chunk of a row is
 // stored at an XOR-swizzled position so that the MFMA operand reads hit
 // distinct LDS banks. V stays row-major in LDS; its transposed A operand
 // is read with ds_read_b64_tr_b16, which hands lane i of each 16-lane group
