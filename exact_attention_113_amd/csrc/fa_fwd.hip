@@ -49,16 +49,24 @@ namespace fa {
 namespace {
 
 // Workgroups of eight waves, one per CU. Each wave takes 32 rows and all of
-// their keys (256 rows per workgroup) when that gives at least kMinGrid
-// workgroups. Otherwise (short sequences) a workgroup takes 128 rows and the
-// two waves of each 32-row group split the keys (KS = 2): the key loop, the
-// critical path of such short grids, halves, and a SIMD still runs two
-// waves. (Four-wave workgroups of 128 rows with whole key ranges, one wave
-// per SIMD, measured 8 % slower at N = 1024 and 15 % at B2 H8 N512 D64.)
+// their keys (256 rows per workgroup) when the grid is large enough: causal
+// attention needs at least kMinGrid such workgroups (two per CU, so that the
+// heavy and light tiles of the causal triangle pair up), full attention,
+// whose workgroups all take equally long, more than kMaxSplitFull (over half
+// the CUs). Otherwise (short grids) a workgroup takes 128 rows and the two
+// waves of each 32-row group split the keys (KS = 2): the key loop, the
+// critical path of such grids, halves, and a SIMD still runs two waves.
+// Measured at B1 H32 D128: causal N = 2048 (256 tiles) 54.9 us split against
+// 57.7 whole, N = 4096 (512 tiles) 133 against 161; full attention N = 1024
+// (128 tiles) 27.1 split against 32.4 whole, N = 1536 (192 tiles) 63.5
+// against 49.8, N = 2048 86.1 against 72.2. (Four-wave workgroups of 128
+// rows with whole key ranges, one wave per SIMD, measured 8 % slower than
+// the split at causal N = 1024 and 15 % at B2 H8 N512 D64.)
 #ifndef FA_FWD_MIN_GRID
 #define FA_FWD_MIN_GRID 512
 #endif
-constexpr int64_t kMinGrid = FA_FWD_MIN_GRID;  // workgroups wanted before splitting keys
+constexpr int64_t kMinGrid = FA_FWD_MIN_GRID;  // causal: workgroups wanted before splitting keys
+constexpr int64_t kMaxSplitFull = 128;         // full attention: largest grid that splits keys
 constexpr int kBN = 64;                 // keys per LDS tile
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
@@ -674,8 +682,8 @@ hipError_t launch_half(const FwdArgs& a) {
     else
       hipLaunchKernelGGL((fwd_kernel<TT, D, 8, false, KS>), grid, dim3(512), 0, a.stream, p);
   };
-  const int64_t bh = a.B * a.H;
-  if (((a.N + 255) / 256) * bh >= kMinGrid) go(std::integral_constant<int, 1>{});
+  const int64_t tiles = ((a.N + 255) / 256) * a.B * a.H;  // 256-row workgroups
+  if (a.causal ? tiles >= kMinGrid : tiles > kMaxSplitFull) go(std::integral_constant<int, 1>{});
   else go(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }

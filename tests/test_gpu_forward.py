@@ -200,3 +200,14 @@ def test_large_grid_d64(causal, shape):
                                     device=DEV)
     check(f"D64 B{B} H{H} N{N} causal={causal}", q, k, v, causal, 0.125, "bf16",
           [(0, 0), (B // 2, 7), (B - 1, H - 1)])
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 1536, 128), (3, 32, 1024, 64), (1, 32, 1024, 128)])
+def test_full_attention_grid_sizes(shape):
+    """Full attention on grids just above and at half the CUs' worth of
+    256-row tiles (whole key ranges above, split keys at or below): sampled
+    heads against the oracle."""
+    B, H, N, D = shape
+    q, k, v = workloads.make_random((B, H, N, D), seed=5100 + N + D, dtype="bf16", device=DEV)
+    check(f"full B{B} H{H} N{N} D{D}", q, k, v, False, D ** -0.5, "bf16",
+          [(0, 0), (B - 1, H // 2), (B - 1, H - 1)])
