@@ -50,23 +50,21 @@ namespace {
 
 // Workgroups of eight waves, one per CU. Each wave takes 32 rows and all of
 // their keys (256 rows per workgroup) when the grid is large enough: causal
-// attention needs at least kMinGrid such workgroups (two per CU, so that the
-// heavy and light tiles of the causal triangle pair up), full attention,
-// whose workgroups all take equally long, more than kMaxSplitFull (over half
-// the CUs). Otherwise (short grids) a workgroup takes 128 rows and the two
-// waves of each 32-row group split the keys (KS = 2): the key loop, the
-// critical path of such grids, halves, and a SIMD still runs two waves.
-// Measured at B1 H32 D128: causal N = 2048 (256 tiles) 54.9 us split against
-// 57.7 whole, N = 4096 (512 tiles) 133 against 161; full attention N = 1024
-// (128 tiles) 27.1 split against 32.4 whole, N = 1536 (192 tiles) 63.5
-// against 49.8, N = 2048 86.1 against 72.2. (Four-wave workgroups of 128
+// attention needs more such workgroups than the 256 CUs (a second round, so
+// that light tiles of the causal triangle follow the heavy ones), full
+// attention, whose workgroups all take equally long, more than half as many.
+// Otherwise (short grids) a workgroup takes 128 rows and the two waves of
+// each 32-row group split the keys (KS = 2): the key loop, the critical path
+// of such grids, halves, and a SIMD still runs two waves. Measured (D128):
+// causal B1 H32 N2048 (256 tiles) 54.9 us split against 57.7 whole; causal
+// grids of 384 tiles 13-19 % faster whole (B1 H48 N2048 81 against 66 us);
+// B1 H32 N4096 (512 tiles) 161 split against 133 whole; full attention B1
+// H32 N1024 (128 tiles) 27.1 split against 32.4 whole, N1536 (192 tiles)
+// 63.4 against 51.2, N2048 88.1 against 73.8. (Four-wave workgroups of 128
 // rows with whole key ranges, one wave per SIMD, measured 8 % slower than
 // the split at causal N = 1024 and 15 % at B2 H8 N512 D64.)
-#ifndef FA_FWD_MIN_GRID
-#define FA_FWD_MIN_GRID 512
-#endif
-constexpr int64_t kMinGrid = FA_FWD_MIN_GRID;  // causal: workgroups wanted before splitting keys
-constexpr int64_t kMaxSplitFull = 128;         // full attention: largest grid that splits keys
+constexpr int64_t kMaxSplitCausal = 256;  // causal: largest grid that splits keys
+constexpr int64_t kMaxSplitFull = 128;    // full attention: largest grid that splits keys
 constexpr int kBN = 64;                 // keys per LDS tile
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
@@ -683,7 +681,7 @@ hipError_t launch_half(const FwdArgs& a) {
       hipLaunchKernelGGL((fwd_kernel<TT, D, 8, false, KS>), grid, dim3(512), 0, a.stream, p);
   };
   const int64_t tiles = ((a.N + 255) / 256) * a.B * a.H;  // 256-row workgroups
-  if (a.causal ? tiles >= kMinGrid : tiles > kMaxSplitFull) go(std::integral_constant<int, 1>{});
+  if (tiles > (a.causal ? kMaxSplitCausal : kMaxSplitFull)) go(std::integral_constant<int, 1>{});
   else go(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }

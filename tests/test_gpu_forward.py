@@ -211,3 +211,14 @@ def test_full_attention_grid_sizes(shape):
     q, k, v = workloads.make_random((B, H, N, D), seed=5100 + N + D, dtype="bf16", device=DEV)
     check(f"full B{B} H{H} N{N} D{D}", q, k, v, False, D ** -0.5, "bf16",
           [(0, 0), (B - 1, H // 2), (B - 1, H - 1)])
+
+
+@pytest.mark.parametrize("shape", [(1, 48, 2048, 128), (3, 32, 1024, 64), (1, 32, 2048, 128)])
+def test_causal_grid_sizes(shape):
+    """Causal attention on grids just above and at one round of the CUs'
+    256-row tiles (whole key ranges above, split keys at or below): sampled
+    heads against the oracle."""
+    B, H, N, D = shape
+    q, k, v = workloads.make_random((B, H, N, D), seed=5300 + N + D, dtype="bf16", device=DEV)
+    check(f"causal B{B} H{H} N{N} D{D}", q, k, v, True, D ** -0.5, "bf16",
+          [(0, 0), (B - 1, H // 2), (B - 1, H - 1)])
