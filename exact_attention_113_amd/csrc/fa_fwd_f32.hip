@@ -28,8 +28,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
   constexpr int VSTR = D;
   constexpr int DB = D / 32;
   constexpr int KK = D / 2;
-  __shared__ float Ks[BN * KSTR];
-  __shared__ float Vs[BN * VSTR];
+  // Two K and two V tiles: tile t + 1 is fetched into registers while tile
+  // t is used, then written to the other buffer (one barrier per tile).
+  __shared__ float Ks[2][BN * KSTR];
+  __shared__ float Vs[2][BN * VSTR];
+  constexpr int PER = BN * D / 4 / kThreads;  // 16-byte pieces per thread and tensor
+  static_assert(PER * kThreads * 4 == BN * D, "tile not divisible among the threads");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -58,24 +62,44 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
+  f32x4 kx[PER], vx[PER];
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c4 = tid + i * kThreads;
+      const int row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+      // Rows past N read row N - 1 and are zeroed when stored.
+      const int grow = min(k0 + row, N - 1);
+      kx[i] = *(const f32x4*)(Kh + (size_t)grow * D + col);
+      vx[i] = *(const f32x4*)(Vh + (size_t)grow * D + col);
+    }
+  };
+  auto stash = [&](int t, int buf) __attribute__((always_inline)) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c4 = tid + i * kThreads;
+      const int row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+      const bool ok = k0 + row < N;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ks[buf][row * KSTR + col + e] = ok ? kx[i][e] : 0.f;
+      *(f32x4*)(&Vs[buf][row * VSTR + col]) = ok ? vx[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (ntiles > 0) {
+    fetch(0);
+    stash(0, 0);
+  }
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
-    __syncthreads();
-    for (int c4 = tid; c4 < BN * D / 4; c4 += kThreads) {
-      const int row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
-      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (k0 + row < N) {
-        kx = *(const f32x4*)(Kh + (size_t)(k0 + row) * D + col);
-        vx = *(const f32x4*)(Vh + (size_t)(k0 + row) * D + col);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Ks[row * KSTR + col + e] = kx[e];
-      *(f32x4*)(Vs + row * VSTR + col) = vx;
-    }
-    __syncthreads();
-
-    const bool active = k0 < N && (!CAUSAL || k0 <= qw0 + 31);
-    if (!active) continue;  // wave-uniform; barriers above are shared by all waves
+    const int buf = t & 1;
+    if (t + 1 < ntiles) fetch(t + 1);
+    const float* Kt = Ks[buf];
+    const float* Vt = Vs[buf];
+    const bool active = k0 < N && (!CAUSAL || k0 <= qw0 + 31);  // wave-uniform
+    if (active) {
     const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw0);
 
     f32x16 s;
@@ -83,7 +107,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[lq * KSTR + 2 * kk + hi], qf[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(Kt[lq * KSTR + 2 * kk + hi], qf[kk], s, 0, 0, 0);
 
     if (need_mask) {
 #pragma unroll
@@ -123,9 +147,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VSTR + 32 * db + lq], p[r],
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vt[key * VSTR + 32 * db + lq], p[r],
                                                         oacc[db], 0, 0, 0);
       }
+    }
+    // Tile t + 1 into the other buffer (its last readers passed the barrier
+    // that ended iteration t - 1), then one barrier for both buffers.
+    if (t + 1 < ntiles) stash(t + 1, buf ^ 1);
+    __syncthreads();
   }
 
   const float ltot = half_swap_sum(lsum);
