@@ -80,7 +80,8 @@ using True = std::true_type;
 struct Unmasked : std::false_type {};
 
 // Work-item order: heavier causal query tiles first (longest job first
-// over the CUs). The (sequence, head) pairs are numbered head-major,
+// over the CUs; in packed batches, round r takes each sequence's r-th tile
+// from its end). The (sequence, head) pairs are numbered head-major,
 // p = h * batch + b; when they divide evenly over the 8 XCDs, each XCD
 // keeps one contiguous range of p: the same heads of every sequence. Their
 // K and V stay in that XCD's L2 (with grouped heads, the query heads of one
@@ -171,7 +172,6 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   const uint32_t qsign = prm.qsign;
   int qt, p;
   tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, qt, p);
-  const int q0 = qt * kBM;
   // This (sequence, head): its length N, the element offsets of its first
   // Q/O and K/V rows and of its LSE entries, and the row strides.
   const int batch = prm.bh_count / prm.heads;
@@ -197,7 +197,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
     lbase = (size_t)bh * N;
     sq = skv = D;
   }
-  if (q0 >= N) return;  // a tile past the end of a shorter sequence: no work
+  // Packed batches count a sequence's tiles back from its own last one, so
+  // that the slots past the end of shorter sequences (no work) come last in
+  // the dispatch order instead of first.
+  if (prm.cu) qt -= prm.n_qtiles - (N + kBM - 1) / kBM;
+  if (qt < 0) return;
+  const int q0 = qt * kBM;
   const uint16_t* Qh = prm.q + qbase;
   const uint16_t* Kh = prm.k + kvbase;
   const uint16_t* Vh = prm.v + kvbase;
