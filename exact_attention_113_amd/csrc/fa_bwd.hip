@@ -196,6 +196,7 @@ struct BwdParams {
   uint32_t qsign;
   DropParams drop;   // dense batches only
   int diag;          // query i sees keys 0 .. i + diag (0: causal; >= N: all)
+  int round_major;   // dQ kernel: work order (see bwd_dq_kernel)
 };
 
 // Where sequence b's rows are: its length, the element offsets of row 0 of
@@ -535,18 +536,40 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   const float dq_scale = prm.grad_scale;
   const uint32_t qsign = prm.qsign;
   const DropParams& drop = prm.drop;
-  // One (sequence b, query head h, query tile): heaviest causal query tiles
-  // first, heads pinned to XCDs, units head-major as in the dK/dV kernel.
-  // Head h reads K/V head h / group.
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int unit = logical / prm.n_tiles;
-  const int qt = prm.n_tiles - 1 - logical % prm.n_tiles;
+  // One (sequence b, query head h, query tile); units (b, h) numbered
+  // head-major, heads pinned to XCDs, heaviest causal query tiles first.
+  // Unit-major (the default): each XCD runs one unit's tiles after another,
+  // which keeps that unit's K/V in its L2. Round-major (grids of at most two
+  // workgroups per CU): round r takes every unit's r-th tile counted back
+  // from the end of its sequence, the forward's order, which pairs heavy and
+  // light tiles on each CU exactly. Head h reads K/V head h / group.
+  int unit, round;
+  if (prm.round_major) {
+    const int units = prm.batch * prm.heads;
+    if ((units & 7) == 0) {
+      const int per_xcd = units >> 3;
+      const int slot = blockIdx.x >> 3;
+      unit = (blockIdx.x & 7) * per_xcd + slot % per_xcd;
+      round = slot / per_xcd;
+    } else {
+      unit = blockIdx.x % units;
+      round = blockIdx.x / units;
+    }
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    unit = logical / prm.n_tiles;
+    round = logical % prm.n_tiles;
+  }
   const int h = unit / prm.batch, bidx = unit - h * prm.batch;
   const int bh = bidx * prm.heads + h;
   const SeqRows sr = seq_rows<D>(prm, bidx, h, h / prm.group);
   const int N = sr.N;
+  // Unit-major counts from the longest sequence's end (its empty slots
+  // then sit at the start of the unit's range), round-major from this
+  // sequence's own end.
+  const int qt = (prm.round_major ? (N + BM - 1) / BM : prm.n_tiles) - 1 - round;
   const int q0 = qt * BM;
-  if (q0 >= N) return;  // a query tile past the end of a shorter sequence
+  if (qt < 0 || q0 >= N) return;  // a slot past the end of a shorter sequence
   LdsOffsets<D> ldo;
   ldo.init(lane);
   const uint16_t* Kh = prm.k + sr.kvbase;
@@ -556,19 +579,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   // operands of S^T = K Q^T and dP^T = V dO^T, and the rows' statistics.
   const int qw0 = q0 + 32 * w;
   const int qi = qw0 + lq;
+  // All loads go out together: rows past N read row N - 1 and are zeroed
+  // afterwards (under a per-row branch the compiler waited for the first
+  // loads before issuing the rest).
+  const bool row_ok = qi < N;
+  const int qc = min(qi, N - 1);
   u32x4 qf[KK], gf[KK];
+  {
+    const size_t roff = sr.qbase + (size_t)qc * sr.qstride + 8 * hi;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (qi < N) {
-      x = *(const u32x4*)(prm.q + sr.qbase + (size_t)qi * sr.qstride + 16 * kk + 8 * hi);
-      y = *(const u32x4*)(prm.dout + sr.qbase + (size_t)qi * sr.qstride + 16 * kk + 8 * hi);
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = *(const u32x4*)(prm.q + roff + 16 * kk);
+      gf[kk] = *(const u32x4*)(prm.dout + roff + 16 * kk);
     }
-    qf[kk] = x ^ qsign;
-    gf[kk] = y;
+    const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = (qf[kk] ^ qsign) & qmask;
+      gf[kk] = gf[kk] & qmask;
+    }
   }
-  const float l2 = qi < N ? prm.lse2[sr.sbase + qi] : 0.f;
-  const float dl = qi < N ? prm.delta[sr.sbase + qi] : 0.f;
+  const float l2r = prm.lse2[sr.sbase + qc], dlr = prm.delta[sr.sbase + qc];
+  const float l2 = row_ok ? l2r : 0.f;
+  const float dl = row_ok ? dlr : 0.f;
 
   f32x16 acc[DB];  // dQ^T: lane = query, register = dim
 #pragma unroll
@@ -718,6 +751,11 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   prm.drop = a.drop;
 
   const int n_ktiles = (int)((a.N + 127) / 128);
+  // dQ grids of at most two workgroups per CU run round-major (measured at
+  // B1 H32 N4096 D128 causal, 512 workgroups: backward 569 against 626-634
+  // us unit-major; at 2048 workgroups and in the packed GQA batch unit-major
+  // was 1.5 % and 5 % faster).
+  constexpr int64_t kMaxRoundMajorDq = 512;
   const int n_qtiles = (int)((a.N + 255) / 256);
   const dim3 g1((unsigned)((int64_t)n_ktiles * a.B * hkv));
   const dim3 g2((unsigned)((int64_t)n_qtiles * a.B * a.H));
@@ -731,6 +769,7 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
     if (err != hipSuccess) return err;
     BwdParams p2 = prm;
     p2.n_tiles = n_qtiles;
+    p2.round_major = (int64_t)g2.x <= kMaxRoundMajorDq;
     hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR>), g2, dim3(kThreads), 0, a.stream, p2);
     return hipGetLastError();
   };
