@@ -196,7 +196,7 @@ struct BwdParams {
   uint32_t qsign;
   DropParams drop;   // dense batches only
   int diag;          // query i sees keys 0 .. i + diag (0: causal; >= N: all)
-  int round_major;   // dQ kernel: work order (see bwd_dq_kernel)
+  int round_major;   // work order of small grids (see each kernel)
 };
 
 // Where sequence b's rows are: its length, the element offsets of row 0 of
@@ -261,11 +261,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   // One (sequence b, K/V head hk, key tile): key tiles with the most query
   // tiles first, heads pinned to XCDs. Units run head-major, so that each
   // XCD's share holds every sequence of a few heads (sequences of unequal
-  // length would otherwise load the XCDs unevenly). The group's query heads
-  // all contribute to this tile's dK and dV.
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int unit = logical / prm.n_tiles;
-  const int kt = logical % prm.n_tiles;
+  // length would otherwise load the XCDs unevenly). Unit-major (the
+  // default): each XCD runs one unit's key tiles after another, sharing its
+  // Q and dO in L2. Round-major (small grids): round r takes key tile r of
+  // every unit, which spreads heavy and light tiles evenly over the CUs. The
+  // group's query heads all contribute to this tile's dK and dV.
+  int unit, kt;
+  if (prm.round_major) {
+    const int units = prm.batch * (prm.heads / prm.group);
+    if ((units & 7) == 0) {
+      const int per_xcd = units >> 3;
+      const int slot = blockIdx.x >> 3;
+      unit = (blockIdx.x & 7) * per_xcd + slot % per_xcd;
+      kt = slot / per_xcd;
+    } else {
+      unit = blockIdx.x % units;
+      kt = blockIdx.x / units;
+    }
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    unit = logical / prm.n_tiles;
+    kt = logical % prm.n_tiles;
+  }
   const int hk = unit / prm.batch, bidx = unit - hk * prm.batch;
   const SeqRows sr0 = seq_rows<D>(prm, bidx, hk * prm.group, hk);
   const int N = sr0.N;
@@ -756,6 +773,8 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   // us unit-major; at 2048 workgroups and in the packed GQA batch unit-major
   // was 1.5 % and 5 % faster).
   constexpr int64_t kMaxRoundMajorDq = 512;
+  // dK/dV grids of at most four workgroups per CU run round-major.
+  constexpr int64_t kMaxRoundMajorDkdv = 1024;
   const int n_qtiles = (int)((a.N + 255) / 256);
   const dim3 g1((unsigned)((int64_t)n_ktiles * a.B * hkv));
   const dim3 g2((unsigned)((int64_t)n_qtiles * a.B * a.H));
@@ -764,6 +783,7 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
     constexpr bool DR = decltype(drop)::value;
     BwdParams p1 = prm;
     p1.n_tiles = n_ktiles;
+    p1.round_major = (int64_t)g1.x <= kMaxRoundMajorDkdv;
     hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR>), g1, dim3(kThreads), 0, a.stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
