@@ -768,12 +768,13 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   prm.drop = a.drop;
 
   const int n_ktiles = (int)((a.N + 127) / 128);
-  // dQ grids of at most two workgroups per CU run round-major (measured at
-  // B1 H32 N4096 D128 causal, 512 workgroups: backward 569 against 626-634
-  // us unit-major; at 2048 workgroups and in the packed GQA batch unit-major
-  // was 1.5 % and 5 % faster).
+  // Causal dQ grids of at most two workgroups per CU run round-major
+  // (measured at B1 H32 N4096 D128, 512 workgroups: backward 569 against
+  // 626-634 us unit-major; at 2048 workgroups and in the packed GQA batch
+  // unit-major was 1.5 % and 5 % faster). Full attention's tiles all cost
+  // the same, so there the order could only change the L2 sharing.
   constexpr int64_t kMaxRoundMajorDq = 512;
-  // dK/dV grids of at most four workgroups per CU run round-major.
+  // Causal dK/dV grids of at most four workgroups per CU run round-major.
   constexpr int64_t kMaxRoundMajorDkdv = 1024;
   const int n_qtiles = (int)((a.N + 255) / 256);
   const dim3 g1((unsigned)((int64_t)n_ktiles * a.B * hkv));
@@ -783,13 +784,13 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
     constexpr bool DR = decltype(drop)::value;
     BwdParams p1 = prm;
     p1.n_tiles = n_ktiles;
-    p1.round_major = (int64_t)g1.x <= kMaxRoundMajorDkdv;
+    p1.round_major = a.causal && (int64_t)g1.x <= kMaxRoundMajorDkdv;
     hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR>), g1, dim3(kThreads), 0, a.stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     BwdParams p2 = prm;
     p2.n_tiles = n_qtiles;
-    p2.round_major = (int64_t)g2.x <= kMaxRoundMajorDq;
+    p2.round_major = a.causal && (int64_t)g2.x <= kMaxRoundMajorDq;
     hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR>), g2, dim3(kThreads), 0, a.stream, p2);
     return hipGetLastError();
   };
