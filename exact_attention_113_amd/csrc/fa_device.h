@@ -135,11 +135,27 @@ __device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], flo
 // key; each round multiplies counter words 0 and 2 by two fixed constants,
 // crosses the high halves into words 1 and 3 with the key, and the key is
 // bumped by two Weyl constants.
+// WIDE forms each 32 x 32 -> 64-bit product with one multiply that gives
+// both halves (one instruction instead of two, but a register pair; the
+// same bits either way).
+template <bool WIDE = false>
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+    uint32_t hi0, lo0, hi1, lo1;
+    if constexpr (WIDE) {
+      const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+      const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+      hi0 = (uint32_t)(p0 >> 32);
+      lo0 = (uint32_t)p0;
+      hi1 = (uint32_t)(p1 >> 32);
+      lo1 = (uint32_t)p1;
+    } else {
+      hi0 = __umulhi(0xD2511F53u, c[0]);
+      lo0 = 0xD2511F53u * c[0];
+      hi1 = __umulhi(0xCD9E8D57u, c[2]);
+      lo1 = 0xCD9E8D57u * c[2];
+    }
     c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
@@ -200,9 +216,10 @@ __device__ __forceinline__ u32x4 byte_transpose(u32x4 x) {
 // block starting at key0; the four lanes of a quad hold rows 4a .. 4a + 3).
 // Bit r of the result is set when element r is kept. Each lane of the quad
 // computes one of the four calls its rows need.
+template <bool WIDE = false>
 __device__ __forceinline__ uint32_t keep_bits_rows(const DropParams& dp, int bh, int row,
                                                    int key0, int hi, int s) {
-  const u32x4 w = philox4x32_10(
+  const u32x4 w = philox4x32_10<WIDE>(
       u32x4{(uint32_t)((key0 >> 2) + 2 * s + hi), (uint32_t)(row >> 2), (uint32_t)bh, dp.offset},
       dp.k0, dp.k1);
   const u32x4 v = quad_transpose(w, s);  // v[m] = word (row % 4) of call m

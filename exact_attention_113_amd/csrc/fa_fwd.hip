@@ -317,7 +317,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   // 1 / (1 - p) at the end.
   auto drop_operand = [&](int b, const float (&p)[16], u32x4 (&pf)[2])
       __attribute__((always_inline)) {
-    const uint32_t bits = keep_bits_rows(prm.drop, bh, qi, kKB * b, hi, lane & 3);
+    const uint32_t bits = keep_bits_rows<true>(prm.drop, bh, qi, kKB * b, hi, lane & 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
