@@ -6,7 +6,8 @@ import torch
 
 import exact_attention_113_amd as fa
 import workloads
-from gpu_util import all_heads, assert_close, oracle_backward, pick, to64
+from gpu_util import (all_heads, assert_close, backward_oracle, compare_heads, oracle_backward,
+                      pick, to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -19,33 +20,62 @@ def run(q, k, v, do, causal, scale):
     return dq, dk, dv
 
 
-def check(name, q, k, v, do, causal, scale, dtype, heads, strict=False):
+def check(name, q, k, v, do, causal, scale, dtype, heads):
     dq, dk, dv = run(q, k, v, do, causal, scale)
     ref = oracle_backward(q, k, v, do, scale, causal, heads)
     for tag, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
-        assert_close(f"{name} {tag}", pick(got, heads), r, dtype, strict=strict)
+        assert_close(f"{name} {tag}", pick(got, heads), r, dtype)
     return dq, dk, dv
 
 
+# Column-sum residues, in units of the standard deviation that rounding to
+# bf16 explains. bf16 keeps 8 significant bits, so its unit roundoff is
+# u = 2^-8: a rounded value carries a relative error of at most u, and
+# (the error being uniform over at most +-u) a standard deviation of at
+# most sigma = u / sqrt(3), independently from element to element.
+#   dV: sum_j dV_j - sum_i dO_i = sum_i dO_i (sum_j P^_ij - 1) + output
+#       rounding, where P^ is P rounded as the dV product's operand, so
+#       var <= sigma^2 (|dO_col|^2 + |dV_col|^2) (rows of P have sum P^2 <= 1).
+#   dK: sum_j dK_j = scale sum_i Q_i (sum_j dS^_ij); with delta taken from
+#       the forward's O, sum_j dS_ij = dO_i . (O_i - O^_i) instead of 0, and
+#       O^ differs from the exact O by the forward's rounding of P (as its
+#       P V operand) and of O itself: two terms of variance about
+#       sigma^2 scale^2 sum_i Q_id^2 |dO_i * O_i|^2 each. The rounding of dS
+#       as the dK operand and of the output dK add sigma^2 |dK_col|^2 each.
+# The bound is a multiple of that deviation taken over all 8192 columns; a
+# masking or indexing error leaves a residue of the order of the column's
+# norm, hundreds of deviations.
+COLSUM_SIGMAS = 8.0
+BF16_U = 2.0 ** -8
+
+
+@pytest.mark.timeout(900)
 def test_bf16_training_b4h16_n8192():
     w = workloads.bf16_training()
     q, k, v, do = workloads.make_inputs(w, device=DEV)
-    dq, dk, dv = check(w.name, q, k, v, do, w.causal, w.scale, w.dtype, [(0, 0), (3, 15)],
-                       strict=True)
-    # Every head, every column: sum_j dV_j = sum_i dO_i (rows of P sum to 1)
-    # and sum_j dK_j = 0 (rows of dS sum to 0). Rounding P and dS to bf16 for
-    # the products, delta taken from the bf16 O, and bf16 outputs leave a
-    # residue far below the columns' norms; a masking or indexing error
-    # leaves one of the order of the norm.
-    sdv = dv.double().sum(dim=2)
-    sdo = do.double().sum(dim=2)
-    nv = dv.double().pow(2).sum(dim=2).sqrt()
-    rv = float(((sdv - sdo).abs() / nv).max())
-    sdk = dk.double().sum(dim=2)
-    nk = dk.double().pow(2).sum(dim=2).sqrt()
-    rk = float((sdk.abs() / nk).max())
-    print(f"max |sum dV - sum dO| / |dV| = {rv:.3e}; max |sum dK| / |dK| = {rk:.3e}", flush=True)
-    assert rv <= 0.05 and rk <= 0.05
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    # Every (batch, head) against the oracle's exact gradient.
+    compare_heads(w.name, (q, k, v, do), backward_oracle(w.scale, w.causal),
+                  [("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)], w.dtype, all_heads(w.B, w.H),
+                  strict=True)
+    # Every column of every head: sum_j dV_j = sum_i dO_i (rows of P sum to
+    # 1) and sum_j dK_j = 0 (rows of dS sum to 0), independent of the oracle.
+    sigma = BF16_U / 3 ** 0.5
+    dv64, do64, dk64, q64, o64 = (t.double() for t in (dv, do, dk, q, o))
+    rv = (dv64.sum(dim=2) - do64.sum(dim=2)).abs() / (
+        sigma * (dv64.pow(2).sum(dim=2) + do64.pow(2).sum(dim=2)).sqrt())
+    t = (do64 * o64).pow(2).sum(dim=3, keepdim=True)
+    var_k = 2 * w.scale ** 2 * (q64.pow(2) * t).sum(dim=2) + 2 * dk64.pow(2).sum(dim=2)
+    rk = dk64.sum(dim=2).abs() / (sigma * var_k.sqrt())
+    qs = torch.tensor([0.5, 0.99, 0.999], dtype=torch.float64, device=DEV)
+    print(f"column sums in sigmas: dV max {float(rv.max()):.2f} quantiles "
+          f"{[round(float(x), 2) for x in torch.quantile(rv.flatten(), qs)]}; dK max "
+          f"{float(rk.max()):.2f} quantiles "
+          f"{[round(float(x), 2) for x in torch.quantile(rk.flatten(), qs)]} "
+          f"(bound {COLSUM_SIGMAS})", flush=True)
+    assert float(rv.max()) <= COLSUM_SIGMAS and float(rk.max()) <= COLSUM_SIGMAS
 
 
 ODD_N = [1, 7, 33, 64, 65, 127, 129, 300]
@@ -172,8 +202,7 @@ def test_batch_independence_odd_key_tiles(causal, D, dropout_p):
         heads = [(0, 0), (1, 17), (3, 31)]
         ref = oracle_backward(q, k, v, do, D ** -0.5, causal, heads)
         for tag, got, r in zip(("dQ", "dK", "dV"), g, ref):
-            assert_close(f"odd tiles D{D} causal={causal} {tag}", pick(got, heads), r, "bf16",
-                         strict=True)
+            assert_close(f"odd tiles D{D} causal={causal} {tag}", pick(got, heads), r, "bf16")
     # The same O and LSE for both: the forward's own grid rule may differ.
     one = [t[:1].contiguous() for t in (q, k, v, o, lse, do)]
     g1 = fa.backward(*one, **kw)

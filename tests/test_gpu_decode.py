@@ -25,7 +25,7 @@ def cache_inputs(B, cap, s_q, H, H_kv, D, dtype, seed):
     return q.to(DEV), k.to(DEV), v.to(DEV)
 
 
-def check(name, o, lse, q, k, v, lens, scale, dtype, strict=False):
+def check(name, o, lse, q, k, v, lens, scale, dtype):
     ro, rl = orc.attention_decode(to64(q), to64(k), to64(v), lens, scale)
     go, gl = to64(o), to64(lse)
     empty = np.isneginf(rl)                       # [B, H, s_q]: rows that see no key
@@ -33,7 +33,7 @@ def check(name, o, lse, q, k, v, lens, scale, dtype, strict=False):
     assert (go.transpose(0, 2, 1, 3)[empty] == 0).all(), name + ": rows without keys not 0"
     seen = ~empty.transpose(0, 2, 1)              # [B, s_q, H]
     if seen.any():
-        assert_close(name + " O", go[seen], ro[seen], dtype, strict=strict)
+        assert_close(name + " O", go[seen], ro[seen], dtype)
         assert_lse_close(name, gl[~empty], rl[~empty])
 
 
@@ -63,7 +63,7 @@ def test_decode_single_chunk():
     q, k, v = cache_inputs(B, cap, 1, 32, 32, 128, "bf16", seed=72)
     o, lse = fa.decode(q, k, v, torch.tensor(lens, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
-    check("single chunk", o, lse, q, k, v, lens, 128 ** -0.5, "bf16", strict=True)
+    check("single chunk", o, lse, q, k, v, lens, 128 ** -0.5, "bf16")
 
 
 def test_decode_lengths_clamped():
@@ -93,7 +93,7 @@ def test_decode_batch_workload():
     q, k, v, lt = workloads.make_decode_inputs(w, device=DEV)
     o, lse = fa.decode(q, k, v, lt, scale=w.scale)
     torch.cuda.synchronize()
-    check("decode batch", o, lse, q, k, v, list(w.lengths), w.scale, "bf16", strict=True)
+    check("decode batch", o, lse, q, k, v, list(w.lengths), w.scale, "bf16")
 
 
 def test_decode_repeatable_and_workspace_reuse():

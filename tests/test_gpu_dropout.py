@@ -10,7 +10,7 @@ import exact_attention_113_amd as fa
 import oracle.attention as orc
 import oracle.rng as rng
 import workloads
-from gpu_util import assert_close, assert_lse_close, to64
+from gpu_util import assert_close, assert_lse_close, compare_heads, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -95,26 +95,33 @@ def test_repeatable_and_offset_changes_bits():
         assert torch.equal(a, b)
 
 
-def test_training_shape_sampled_head():
-    """The training shape (B4 H16 N8192 D128 causal) with p = 0.1: one head's
-    forward and gradients against the oracle at full length."""
+@pytest.mark.timeout(900)
+def test_training_shape_heads():
+    """The training shape (B4 H16 N8192 D128 causal) with p = 0.1: eight
+    heads, one in each XCD's range of the head-major work order and at a
+    different position in it, forward and gradients against the oracle at
+    full length."""
     w = workloads.bf16_training()
     q, k, v, do = workloads.make_inputs(w, device=DEV)
     kw = dict(causal=True, scale=w.scale, dropout_p=0.1, seed=2024, offset=7)
     o, lse = fa.forward(q, k, v, **kw)
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, **kw)
     torch.cuda.synchronize()
-    b, h = 2, 9
-    sl = lambda t: to64(t[b:b + 1, h:h + 1])
-    bh0 = b * w.H + h
-    ro, rl = orc.attention_forward_dropout(sl(q), sl(k), sl(v), w.scale, True, 0.1, 2024, 7,
-                                           bh0=bh0)
-    assert_close("train dropout O", sl(o), ro, "bf16", strict=True)
-    assert_lse_close("train dropout", sl(lse), rl)
-    grads = orc.attention_backward_dropout(sl(q), sl(k), sl(v), sl(do), w.scale, True, 0.1,
-                                           2024, 7, bh0=bh0)
-    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), grads):
-        assert_close(f"train dropout {name}", sl(g), r, "bf16", strict=True)
+    # Work item p = h * B + b; XCD x takes p in [8x, 8x + 8).
+    heads = [((9 * x) % w.B, (9 * x) // w.B) for x in range(8)]
+
+    def fwd(q1, k1, v1, head):
+        return orc.attention_forward_dropout(q1, k1, v1, w.scale, True, 0.1, 2024, 7,
+                                             bh0=head[0] * w.H + head[1])
+
+    def bwd(q1, k1, v1, do1, head):
+        return orc.attention_backward_dropout(q1, k1, v1, do1, w.scale, True, 0.1, 2024, 7,
+                                              bh0=head[0] * w.H + head[1])
+
+    compare_heads("train dropout", (q, k, v), fwd, [("O", o, 0)], "bf16", heads,
+                  lse=(lse, 1), pass_head=True)
+    compare_heads("train dropout", (q, k, v, do), bwd,
+                  [("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)], "bf16", heads, pass_head=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -7,7 +7,8 @@ import torch
 
 import exact_attention_113_amd as fa
 import workloads
-from gpu_util import (all_heads, assert_close, assert_lse_close, oracle_forward, pick, to64)
+from gpu_util import (all_heads, assert_close, assert_lse_close, compare_heads, forward_oracle,
+                      oracle_forward, pick, to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -27,6 +28,16 @@ def check(name, q, k, v, causal, scale, dtype, heads, strict=False):
     return o, lse
 
 
+def check_every_head(name, q, k, v, causal, scale, dtype):
+    """Every (batch, head) of O and LSE of a named workload against the
+    oracle (threads over heads), at the fixed bars."""
+    o, lse = run(q, k, v, causal, scale)
+    B, H = q.shape[:2]
+    compare_heads(name, (q, k, v), forward_oracle(scale, causal), [("O", o, 0)], dtype,
+                  all_heads(B, H), lse=(lse, 1), strict=True)
+    return o, lse
+
+
 def test_fp32_b1h2_n256_d64():
     w = workloads.fp32_small()
     q, k, v = workloads.make_inputs(w, device=DEV)
@@ -42,27 +53,26 @@ def test_bf16_b2h8_n512_d64():
 def test_fp16_causal_b1h32_n4096_d128():
     w = workloads.fp16_causal_4k()
     q, k, v = workloads.make_inputs(w, device=DEV)
-    o, _ = check(w.name, q, k, v, w.causal, w.scale, w.dtype, [(0, 0), (0, 13), (0, 31)],
-                 strict=True)
-    # Every head: causal row 0 attends to key 0 only, so O[0] = V[0] exactly.
+    o, _ = check_every_head(w.name, q, k, v, w.causal, w.scale, w.dtype)
+    # Causal row 0 attends to key 0 only, so O[0] = V[0] exactly.
     assert torch.equal(o[:, :, 0], v[:, :, 0])
     assert torch.isfinite(o).all()
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("w", workloads.bf16_causal_sweep(), ids=lambda w: w.name)
 def test_bf16_causal_sweep(w):
     q, k, v = workloads.make_inputs(w, device=DEV)
-    heads = [(0, 0), (0, 31)] if w.N <= 8192 else [(0, 17)]
-    o, _ = check(w.name, q, k, v, w.causal, w.scale, w.dtype, heads, strict=True)
+    o, _ = check_every_head(w.name, q, k, v, w.causal, w.scale, w.dtype)
     assert torch.equal(o[:, :, 0], v[:, :, 0])
     assert torch.isfinite(o).all()
 
 
+@pytest.mark.timeout(600)
 def test_bf16_training_forward_b4h16_n8192():
     w = workloads.bf16_training()
     q, k, v = workloads.make_inputs(w, with_grad_out=False, device=DEV)
-    o, _ = check(w.name + " fwd", q, k, v, w.causal, w.scale, w.dtype, [(0, 0), (3, 15)],
-                 strict=True)
+    o, _ = check_every_head(w.name + " fwd", q, k, v, w.causal, w.scale, w.dtype)
     assert torch.equal(o[:, :, 0], v[:, :, 0])
 
 
@@ -162,7 +172,7 @@ def test_long_sequence_sampled_rows():
         ro, rl = orc.attention_decode(to64(q[0, h, i:i + 1])[None, :, None],
                                       to64(k[0, h, :i + 1])[None, :, None],
                                       to64(v[0, h, :i + 1])[None, :, None], [i + 1], D ** -0.5)
-        assert_close(f"head {h} row {i} O", to64(o[0, h, i]), ro[0, 0, 0], "bf16", strict=True)
+        assert_close(f"head {h} row {i} O", to64(o[0, h, i]), ro[0, 0, 0], "bf16")
         assert_lse_close(f"head {h} row {i}", to64(lse[0, h, i:i + 1]), rl[0, 0])
 
 
@@ -182,7 +192,7 @@ def test_offsets_beyond_2g_elements():
     torch.cuda.synchronize()
     heads = [(0, 0), (2048, 5), (4095, 31)]
     ro, rl = oracle_forward(q, k, v, D ** -0.5, True, heads)
-    assert_close("O", pick(o, heads), ro, "bf16", strict=True)
+    assert_close("O", pick(o, heads), ro, "bf16")
     assert_lse_close("LSE", pick(lse, heads), rl)
     for tag, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv),
                            oracle_backward(q, k, v, do, D ** -0.5, True, heads)):

@@ -28,7 +28,7 @@ def packed(lengths, H, H_kv, D, dtype, seed, extra=0):
     return q.to(DEV), k.to(DEV), v.to(DEV), cu
 
 
-def run_and_check(name, q, k, v, cu, causal, scale, dtype, strict=False):
+def run_and_check(name, q, k, v, cu, causal, scale, dtype):
     cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
     lengths = [b - a for a, b in zip(cu[:-1], cu[1:])]
     o, lse = fa.forward_varlen(q, k, v, cu_t, max(lengths), causal=causal, scale=scale)
@@ -37,7 +37,7 @@ def run_and_check(name, q, k, v, cu, causal, scale, dtype, strict=False):
     covered = np.zeros(q.shape[0], dtype=bool)
     for a, b in zip(cu[:-1], cu[1:]):
         covered[a:b] = True
-    assert_close(name + " O", to64(o)[covered], ro[covered], dtype, strict=strict)
+    assert_close(name + " O", to64(o)[covered], ro[covered], dtype)
     assert_lse_close(name, to64(lse)[:, covered], rl[:, covered])
     return o, lse
 
@@ -95,8 +95,7 @@ def test_prefill_batch_workload_sampled():
         hk = h // (w.H // w.H_kv)
         ro, rl = orc.attention_forward(to64(q[s0:s1, h])[None, None], to64(k[s0:s1, hk])[None, None],
                                        to64(v[s0:s1, hk])[None, None], w.scale, True)
-        assert_close(f"seq {b} head {h} O", to64(o[s0:s1, h])[None, None], ro, "bf16",
-                     strict=True)
+        assert_close(f"seq {b} head {h} O", to64(o[s0:s1, h])[None, None], ro, "bf16")
         assert_lse_close(f"seq {b} head {h}", to64(lse[h, s0:s1])[None, None], rl)
 
 

@@ -131,7 +131,7 @@ def test_prefill_batch_workload_sampled():
             to64(q[s0:s1, hs]), to64(k[s0:s1, hk:hk + 1]), to64(v[s0:s1, hk:hk + 1]),
             to64(do[s0:s1, hs]), [0, s1 - s0], w.scale, True)
         name = f"seq {b} (n={s1 - s0}) K/V head {hk}"
-        assert_close(name + " dQ", to64(dq[s0:s1, hs]), rq, "bf16", strict=True)
+        assert_close(name + " dQ", to64(dq[s0:s1, hs]), rq, "bf16")
         # dK and dV sum the contributions of four query heads, so their
         # largest entries reach 4..8, where rounding the exact value to bf16
         # alone costs up to 1/64: the max-abs bar is widened by twice that
