@@ -46,6 +46,33 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k, v must be on one device")
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A tensor handed to a kernel as a raw pointer: it must be contiguous,
+    of the given shape and dtype, on `device` (the inputs' GPU). Anything
+    else would let a kernel read or write outside the tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(name, t, need, device):
+    """A caller's workspace: uint8, contiguous, on `device`, at least `need`
+    bytes (the library also checks the byte count it is given)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device or t.dtype != torch.uint8 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D uint8 tensor on {device}")
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {need} needed")
+
+
 def default_scale(D):
     return 1.0 / math.sqrt(D)
 
@@ -63,8 +90,10 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, dropout_p=0.0
         scale = default_scale(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("out", out, q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer("lse", lse, (B, H, N), torch.float32, q.device)
     lib = _lib.load()
     with torch.cuda.device(q.device):
         if dropout_p:
@@ -87,6 +116,10 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, ou
 
     q: [total, H, D]; k, v: [total, H_kv, D] (H_kv divides H); cu_seqlens: int32
     [batch + 1] on q's device, sequence b being tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
+    max_seqlen sizes the grid and must be at least the longest sequence: the
+    offsets stay on the device (no synchronisation), so a longer sequence is
+    not detected; it is cut to its first max_seqlen tokens and its later rows
+    are not written.
     Returns (o [total, H, D], lse fp32 [H, total]).
     """
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[0] != k.shape[0] \
@@ -101,13 +134,17 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, ou
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be int32 [batch + 1]")
+    if not (q.device == k.device == v.device == cu_seqlens.device):
+        raise ValueError("q, k, v and cu_seqlens must be on one device")
     total, H, D = q.shape
     if scale is None:
         scale = default_scale(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("out", out, q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    _check_buffer("lse", lse, (H, total), torch.float32, q.device)
     lib = _lib.load()
     with torch.cuda.device(q.device):
         st = lib.fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -146,17 +183,23 @@ def decode(q, k_cache, v_cache, cache_seqlens, max_seqlen_k=None, scale=None, ou
     cap, H_kv = k_cache.shape[1], k_cache.shape[2]
     if cache_seqlens.dtype != torch.int32 or cache_seqlens.shape != (B,):
         raise ValueError("cache_seqlens must be int32 [B]")
+    if not (q.device == k_cache.device == v_cache.device == cache_seqlens.device):
+        raise ValueError("q, the caches and cache_seqlens must be on one device")
     if max_seqlen_k is None:
         max_seqlen_k = cap
     if scale is None:
         scale = default_scale(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("out", out, q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+    _check_buffer("lse", lse, (B, H, s_q), torch.float32, q.device)
     need = decode_workspace_bytes(B, s_q, H, H_kv, max_seqlen_k, D)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_workspace("workspace", workspace, need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() if workspace is not None else 0
     lib = _lib.load()
@@ -182,21 +225,21 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, drop
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must match q (shape, dtype, device, contiguous)")
     B, H, N, D = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    _check_buffer("lse", lse, (B, H, N), torch.float32, q.device)
+    for name, t in (("o", o), ("do", do)):
+        _check_buffer(name, t, q.shape, q.dtype, q.device)
     if scale is None:
         scale = default_scale(D)
     need = backward_workspace_bytes(B, H, N, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace("workspace", workspace, need, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
         for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-            if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or \
-                    not t.is_contiguous():
-                raise ValueError(f"{name} must match q (shape, dtype, device, contiguous)")
+            _check_buffer(name, t, q.shape, q.dtype, q.device)
     lib = _lib.load()
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
@@ -233,8 +276,10 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, s
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     total, H, D = q.shape
-    if lse.shape != (H, total) or lse.dtype != torch.float32:
-        raise ValueError("lse must be fp32 [H, total]")
+    _check_buffer("lse", lse, (H, total), torch.float32, q.device)
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("cu_seqlens", cu_seqlens)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be int32 [batch + 1]")
     if scale is None:
@@ -242,14 +287,13 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, s
     need = backward_workspace_bytes(1, H, total, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace("workspace", workspace, need, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
         for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-            if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_cuda or \
-                    not t.is_contiguous():
-                raise ValueError(f"{name} must match its input (shape, dtype, contiguous GPU)")
+            _check_buffer(name, t, ref.shape, ref.dtype, q.device)
     lib = _lib.load()
     with torch.cuda.device(q.device):
         st = lib.fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
