@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa_internal.h"
 
 namespace {
@@ -105,11 +107,12 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   return hip_status(fa::launch_forward(a), who);
 }
 
-fa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
-                        int64_t D, float scale, int causal, int dtype, void* stream,
-                        const fa::DropParams& drop, const char* who) {
+// Checks of a dense backward call except its workspace; on success ws holds
+// the workspace layout the call needs.
+fa_status check_backward(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t N, int64_t D, float scale, int dtype,
+                         const char* who, fa::BwdWorkspace* ws) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return fail(FA_ERR_INVALID_ARGUMENT,
                 "%s: q, k, v, o, dout, lse, dq, dk, dv must be non-NULL", who);
@@ -120,9 +123,20 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   fa_status s = check_shape(B, H, N, D, scale, dtype);
   if (s != FA_OK) return s;
   if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: fp32 backward is not supported", who);
-  fa::BwdWorkspace ws;
-  if (!fa::backward_workspace_layout(B, H, N, D, &ws))
+  if (!fa::backward_workspace_layout(B, H, N, D, ws))
     return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace size overflows", who);
+  return FA_OK;
+}
+
+fa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                        int64_t D, float scale, int causal, int dtype, void* stream,
+                        const fa::DropParams& drop, const char* who) {
+  fa::BwdWorkspace ws;
+  fa_status s = check_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, dtype, who,
+                               &ws);
+  if (s != FA_OK) return s;
   if (!workspace)
     return fail(FA_ERR_WORKSPACE, "%s: workspace is NULL (needs %lld bytes)", who,
                 (long long)ws.total);
@@ -178,6 +192,53 @@ fa_status check_varlen(int64_t batch, int64_t max_seqlen, int64_t total, int64_t
   const int64_t wgs = ((max_seqlen + 127) / 128) * batch * H;
   if (batch > (int64_t)1 << 30 || wgs > (int64_t)0x7fffffff)
     return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed one grid", who, (long long)wgs);
+  return FA_OK;
+}
+
+// ---- scratch of the allocation-free backward ----------------------------
+// The backward's two fp32 row statistics (delta and LSE * log2 e), laid out
+// as in a caller's workspace, for calls whose workspace would exceed no more
+// than kScratchBytes (B * H * N up to 2^21 rows). Each GPU the library runs
+// on holds its own copy until the process ends. In host code `scratch` only
+// names the symbol: its device address, different on every GPU, comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` runs on (which must be
+// the current device).
+fa_status scratch_address(void* stream, void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, who);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return hip_status(e, who);
+    if ((int)sdev != dev)
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s: the stream runs on device %d, device %d is current",
+                  who, (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "%s: device index %d above %d", who, dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, who);
+    if (!p || misaligned(p, 256))
+      return fail(FA_ERR_HIP, "%s: scratch address %p unusable", who, p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return FA_OK;
 }
 
@@ -289,6 +350,29 @@ fa_status fa_backward_varlen(const void* q, const void* k, const void* v, const 
   fa::BwdArgs a{q,     k,      v,     o,      dout,  lse,       dq,        dk,
                 dv,    workspace, batch, H,     max_seqlen, D,  scale,     causal,
                 dtype, (hipStream_t)stream, fa::DropParams{}, H_kv, cu_seqlens, total};
+  return hip_status(fa::launch_backward(a, ws), who);
+}
+
+fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                              int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  const char* who = "fa_backward_noalloc";
+  fa::BwdWorkspace ws;
+  fa_status s = check_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, dtype, who,
+                               &ws);
+  if (s != FA_OK) return s;
+  if (ws.total > kScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "%s: B*H*N = %lld rows need %lld bytes of scratch, above the %lld this entry "
+                "point holds (use fa_backward with a workspace)",
+                who, (long long)(B * H * N), (long long)ws.total, (long long)kScratchBytes);
+  void* ptr = nullptr;
+  s = scratch_address(stream, &ptr, who);
+  if (s != FA_OK) return s;
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ptr, B, H, N, D, scale, causal, dtype,
+                (hipStream_t)stream, fa::DropParams{}};
   return hip_status(fa::launch_backward(a, ws), who);
 }
 

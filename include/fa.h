@@ -29,7 +29,8 @@
  *   Memory     Every tensor pointer is device memory owned by the caller,
  *              16-byte aligned. The library never allocates, frees or
  *              synchronises, and keeps no state between calls except the
- *              per-thread error text of fa_last_error.
+ *              per-thread error text of fa_last_error and the static
+ *              scratch array of fa_backward_noalloc.
  *   Stream     Work is enqueued on `stream` (a hipStream_t; NULL means the
  *              default stream) and runs asynchronously; a returned FA_OK
  *              means the launch was accepted.
@@ -308,6 +309,30 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
                     size_t workspace_bytes, int64_t batch, int64_t s_q, int64_t cache_capacity,
                     int64_t max_seqlen_k, int64_t H, int64_t H_kv, int64_t D, float scale,
                     int dtype, void* stream);
+
+/*
+ * fa_backward_noalloc - fa_backward without a caller workspace, for callers
+ * that cannot allocate device memory at all (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as fa_backward with dropout off, minus
+ * workspace and workspace_bytes. The two fp32 row statistics the backward
+ * needs live in a static 16 MiB array inside the library instead, one copy
+ * per GPU, held until the process ends: B * H * N may be at most 2^21 rows
+ * (the size fa_backward_workspace_bytes reports must not exceed 16 MiB);
+ * larger calls return FA_ERR_UNSUPPORTED and write nothing. The call
+ * allocates and frees nothing; its first call on a device looks up that
+ * device's copy of the array (stream must run on the current device).
+ * Every call on one GPU shares the array and leaves its contents behind
+ * (each call writes every statistic it reads, so nothing needs clearing):
+ * calls that overlap on one GPU, on different streams, race.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                              int dtype, void* stream);
 
 /* fa_status_string - static, never-NULL name of a status code. */
 const char* fa_status_string(int status);

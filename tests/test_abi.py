@@ -264,3 +264,20 @@ def test_backward_dropout_validation():
     assert lib.fa_backward_dropout(*base, 0.2, 0, 1 << 33, None) == _lib.FA_ERR_INVALID_ARGUMENT
     base[9] = None
     assert lib.fa_backward_dropout(*base, 0.2, 0, 0, None) == _lib.FA_ERR_WORKSPACE
+
+
+def test_backward_noalloc_rejects_before_any_device_work():
+    """The allocation-free backward validates like fa_backward and refuses
+    calls whose statistics exceed its 16 MiB scratch (2^21 rows), all before
+    the first HIP call."""
+    lib = _lib.load()
+
+    def call(B=1, H=1, N=16, D=64, dtype=2, q=A):
+        return lib.fa_backward_noalloc(q, A, A, A, A, A, A, A, A, B, H, N, D, 0.125, 1, dtype,
+                                       None)
+    assert call(q=None) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert call(dtype=0) == _lib.FA_ERR_UNSUPPORTED
+    assert call(D=80) == _lib.FA_ERR_UNSUPPORTED
+    assert call(B=1, H=256, N=8192 + 1) == _lib.FA_ERR_UNSUPPORTED
+    assert "scratch" in _lib.last_error()
+    assert call(B=3, H=1 << 20, N=1) == _lib.FA_ERR_UNSUPPORTED
