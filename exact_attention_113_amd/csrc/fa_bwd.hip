@@ -211,9 +211,8 @@ __device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b, int h, in
   SeqRows r;
   const int hkv = p.heads / p.group;
   if (p.cu) {
-    const int s0 = min(max(p.cu[b], 0), p.total);
-    const int s1 = min(max(p.cu[b + 1], s0), p.total);
-    r.N = min(s1 - s0, p.seqlen);
+    int s0;
+    seq_span(p.cu, b, p.total, p.seqlen, s0, r.N);
     r.qbase = ((size_t)s0 * p.heads + h) * D;
     r.qstride = (size_t)p.heads * D;
     r.kvbase = ((size_t)s0 * hkv + hk) * D;
@@ -234,7 +233,7 @@ __device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b, int h, in
 
 template <typename TT, int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams prm) {
-  constexpr int BK = 128;                // keys per workgroup: 32 per wave pair
+  constexpr int BK = kBwdKeyTile;        // keys per workgroup: 32 per wave pair
   constexpr int BM = 64;                 // query rows per iteration
   constexpr int ROWB = 2 * D;
   constexpr int TILEB = BM * ROWB;
@@ -267,22 +266,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   // every unit, which spreads heavy and light tiles evenly over the CUs. The
   // group's query heads all contribute to this tile's dK and dV.
   int unit, kt;
-  if (prm.round_major) {
-    const int units = prm.batch * (prm.heads / prm.group);
-    if ((units & 7) == 0) {
-      const int per_xcd = units >> 3;
-      const int slot = blockIdx.x >> 3;
-      unit = (blockIdx.x & 7) * per_xcd + slot % per_xcd;
-      kt = slot / per_xcd;
-    } else {
-      unit = blockIdx.x % units;
-      kt = blockIdx.x / units;
-    }
-  } else {
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    unit = logical / prm.n_tiles;
-    kt = logical % prm.n_tiles;
-  }
+  bwd_unit_slot(blockIdx.x, gridDim.x, prm.round_major != 0, prm.batch * (prm.heads / prm.group),
+                prm.n_tiles, unit, kt);
   const int hk = unit / prm.batch, bidx = unit - hk * prm.batch;
   const SeqRows sr0 = seq_rows<D>(prm, bidx, hk * prm.group, hk);
   const int N = sr0.N;
@@ -535,7 +520,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 
 template <typename TT, int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm) {
-  constexpr int BM = 32 * kWaves;  // query rows per workgroup
+  constexpr int BM = kBwdQueryTile;  // query rows per workgroup: 32 per wave
+  static_assert(BM == 32 * kWaves, "one 32-row block per wave");
   constexpr int BN = 64;           // keys per LDS tile
   constexpr int ROWB = 2 * D;
   constexpr int TILEB = BN * ROWB;
@@ -561,22 +547,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   // from the end of its sequence, the forward's order, which pairs heavy and
   // light tiles on each CU exactly. Head h reads K/V head h / group.
   int unit, round;
-  if (prm.round_major) {
-    const int units = prm.batch * prm.heads;
-    if ((units & 7) == 0) {
-      const int per_xcd = units >> 3;
-      const int slot = blockIdx.x >> 3;
-      unit = (blockIdx.x & 7) * per_xcd + slot % per_xcd;
-      round = slot / per_xcd;
-    } else {
-      unit = blockIdx.x % units;
-      round = blockIdx.x / units;
-    }
-  } else {
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    unit = logical / prm.n_tiles;
-    round = logical % prm.n_tiles;
-  }
+  bwd_unit_slot(blockIdx.x, gridDim.x, prm.round_major != 0, prm.batch * prm.heads, prm.n_tiles,
+                unit, round);
   const int h = unit / prm.batch, bidx = unit - h * prm.batch;
   const int bh = bidx * prm.heads + h;
   const SeqRows sr = seq_rows<D>(prm, bidx, h, h / prm.group);
@@ -584,9 +556,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   // Unit-major counts from the longest sequence's end (its empty slots
   // then sit at the start of the unit's range), round-major from this
   // sequence's own end.
-  const int qt = (prm.round_major ? (N + BM - 1) / BM : prm.n_tiles) - 1 - round;
+  const int qt = bwd_dq_tile(round, prm.round_major != 0, prm.n_tiles, N, BM);
+  if (qt < 0) return;  // a slot past the end of a shorter sequence
   const int q0 = qt * BM;
-  if (qt < 0 || q0 >= N) return;  // a slot past the end of a shorter sequence
   LdsOffsets<D> ldo;
   ldo.init(lane);
   const uint16_t* Kh = prm.k + sr.kvbase;
@@ -767,30 +739,22 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
   prm.qsign = qsign;
   prm.drop = a.drop;
 
-  const int n_ktiles = (int)((a.N + 127) / 128);
-  // Causal dQ grids of at most two workgroups per CU run round-major
-  // (measured at B1 H32 N4096 D128, 512 workgroups: backward 569 against
-  // 626-634 us unit-major; at 2048 workgroups and in the packed GQA batch
-  // unit-major was 1.5 % and 5 % faster). Full attention's tiles all cost
-  // the same, so there the order could only change the L2 sharing.
-  constexpr int64_t kMaxRoundMajorDq = 512;
-  // Causal dK/dV grids of at most four workgroups per CU run round-major.
-  constexpr int64_t kMaxRoundMajorDkdv = 1024;
-  const int n_qtiles = (int)((a.N + 255) / 256);
-  const dim3 g1((unsigned)((int64_t)n_ktiles * a.B * hkv));
-  const dim3 g2((unsigned)((int64_t)n_qtiles * a.B * a.H));
+  // Grids and work orders (round-major for small causal grids): bwd_shape.
+  const BwdShape sh = bwd_shape(a.B, a.H, hkv, a.N, a.causal != 0);
+  const dim3 g1((unsigned)sh.grid_dkdv);
+  const dim3 g2((unsigned)sh.grid_dq);
   prm.diag = a.causal ? 0 : (int)a.N;
   auto go = [&](auto drop) -> hipError_t {
     constexpr bool DR = decltype(drop)::value;
     BwdParams p1 = prm;
-    p1.n_tiles = n_ktiles;
-    p1.round_major = a.causal && (int64_t)g1.x <= kMaxRoundMajorDkdv;
+    p1.n_tiles = sh.n_ktiles;
+    p1.round_major = sh.rm_dkdv;
     hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR>), g1, dim3(kThreads), 0, a.stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     BwdParams p2 = prm;
-    p2.n_tiles = n_qtiles;
-    p2.round_major = a.causal && (int64_t)g2.x <= kMaxRoundMajorDq;
+    p2.n_tiles = sh.n_qtiles;
+    p2.round_major = sh.rm_dq;
     hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR>), g2, dim3(kThreads), 0, a.stream, p2);
     return hipGetLastError();
   };

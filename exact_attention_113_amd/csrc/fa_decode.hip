@@ -128,11 +128,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecParams 
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hi = lane >> 5;
 
-  int lin = blockIdx.x;
-  const int split = lin % prm.n_splits;
-  lin /= prm.n_splits;
-  const int hk = lin % prm.hkv;
-  const int b = lin / prm.hkv;
+  int b, hk, split;
+  decode_unit(blockIdx.x, prm.n_splits, prm.hkv, b, hk, split);
   const int L = min(max(prm.seqlens[b], 0), prm.max_len);
   const int k_lo = split * prm.chunk;
   const int k_hi = min(L, k_lo + prm.chunk);
@@ -478,37 +475,6 @@ hipError_t launch_typed(const DecodeArgs& a, const DecodePlan& plan) {
 }
 
 }  // namespace
-
-bool decode_plan(int64_t B, int64_t s_q, int64_t H, int64_t H_kv, int64_t max_len, int64_t D,
-                 DecodePlan* plan) {
-  if (B < 1 || s_q < 1 || H < 1 || H_kv < 1 || max_len < 0 || D < 1) return false;
-  // Enough workgroups to fill the chip a few times over, chunks of at least
-  // 128 keys (one block per wave), at most kMaxSplits chunks per row.
-  const int64_t units = B * H_kv;
-  const int64_t want = (kDecodeTargetWgs + units - 1) / units;
-  const int64_t most = max_len > 0 ? (max_len + 127) / 128 : 1;
-  int64_t n = want < most ? want : most;
-  if (n > kMaxSplits) n = kMaxSplits;
-  if (n < 1) n = 1;
-  int64_t chunk = max_len > 0 ? (max_len + n - 1) / n : 128;
-  chunk = (chunk + 127) / 128 * 128;
-  n = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
-  plan->n_splits = (int)n;
-  plan->chunk = (int)chunk;
-  auto pad = [](size_t x) { return (x + 255) / 256 * 256; };
-  if (n > 1) {
-    const size_t rows = (size_t)B * H * s_q;
-    plan->part_o_off = 0;
-    plan->part_o_bytes = pad(rows * n * D * 4);
-    plan->part_lse_off = plan->part_o_bytes;
-    plan->part_lse_bytes = pad(rows * n * 4);
-    plan->total = plan->part_o_bytes + plan->part_lse_bytes;
-  } else {
-    plan->part_o_off = plan->part_o_bytes = plan->part_lse_off = plan->part_lse_bytes = 0;
-    plan->total = 0;
-  }
-  return true;
-}
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan) {
   const bool bf = a.dtype == FA_BF16;

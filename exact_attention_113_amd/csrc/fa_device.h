@@ -244,13 +244,4 @@ __device__ __forceinline__ uint32_t keep_bits_keys(const DropParams& dp, int bh,
   return bits;
 }
 
-// Map a linear workgroup id to a logical one so that runs of consecutive
-// logical ids land on one XCD. Workgroups are dealt to the 8 XCDs round
-// robin by linear id; when the grid is a multiple of 8, logical id
-// (x * total/8 + s) is given to the s-th workgroup of XCD x.
-__device__ __forceinline__ int xcd_logical_id(int lin, int total) {
-  if ((total & 7) != 0) return lin;
-  return (lin & 7) * (total >> 3) + (lin >> 3);
-}
-
 }  // namespace fa

@@ -63,8 +63,7 @@ namespace {
 // 63.4 against 51.2, N2048 88.1 against 73.8. (Four-wave workgroups of 128
 // rows with whole key ranges, one wave per SIMD, measured 8 % slower than
 // the split at causal N = 1024 and 15 % at B2 H8 N512 D64.)
-constexpr int64_t kMaxSplitCausal = 256;  // causal: largest grid that splits keys
-constexpr int64_t kMaxSplitFull = 128;    // full attention: largest grid that splits keys
+// (The grid rule, kMaxSplitCausal and kMaxSplitFull, is fwd_shape in fa_sched.h.)
 constexpr int kBN = 64;                 // keys per LDS tile
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
@@ -78,26 +77,6 @@ using True = std::true_type;
 // Softmax kind of a step: False = interior block, True = block with masked
 // keys, Unmasked = full softmax without masks (a row's first block).
 struct Unmasked : std::false_type {};
-
-// Work-item order: heavier causal query tiles first (longest job first
-// over the CUs; in packed batches, round r takes each sequence's r-th tile
-// from its end). The (sequence, head) pairs are numbered head-major,
-// p = h * batch + b; when they divide evenly over the 8 XCDs, each XCD
-// keeps one contiguous range of p: the same heads of every sequence. Their
-// K and V stay in that XCD's L2 (with grouped heads, the query heads of one
-// K/V head land together), and sequences of unequal length spread over all
-// XCDs instead of loading some more than others.
-__device__ __forceinline__ void tile_of(int lin, int n_qtiles, int bh_count, int& qt, int& p) {
-  if ((bh_count & 7) == 0) {
-    const int hpx = bh_count >> 3;
-    const int xcd = lin & 7, slot = lin >> 3;
-    qt = n_qtiles - 1 - slot / hpx;
-    p = xcd * hpx + slot % hpx;
-  } else {
-    qt = n_qtiles - 1 - lin / bh_count;
-    p = lin % bh_count;
-  }
-}
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -171,7 +150,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   const float c = prm.c;
   const uint32_t qsign = prm.qsign;
   int qt, p;
-  tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, qt, p);
+  fwd_tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, qt, p);
   // This (sequence, head): its length N, the element offsets of its first
   // Q/O and K/V rows and of its LSE entries, and the row strides.
   const int batch = prm.bh_count / prm.heads;
@@ -182,9 +161,8 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   size_t qbase, kvbase, lbase;
   size_t sq, skv;
   if (prm.cu) {
-    const int s0 = min(max(prm.cu[bidx], 0), prm.total);
-    const int s1 = min(max(prm.cu[bidx + 1], s0), prm.total);
-    N = min(s1 - s0, prm.seqlen);
+    int s0;
+    seq_span(prm.cu, bidx, prm.total, prm.seqlen, s0, N);
     qbase = ((size_t)s0 * prm.heads + h) * D;
     kvbase = ((size_t)s0 * hkv + hk) * D;
     lbase = (size_t)h * prm.total + s0;
@@ -200,7 +178,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   // Packed batches count a sequence's tiles back from its own last one, so
   // that the slots past the end of shorter sequences (no work) come last in
   // the dispatch order instead of first.
-  if (prm.cu) qt -= prm.n_qtiles - (N + kBM - 1) / kBM;
+  qt = fwd_seq_tile(qt, prm.n_qtiles, N, kBM, prm.cu != nullptr);
   if (qt < 0) return;
   const int q0 = qt * kBM;
   const uint16_t* Qh = prm.q + qbase;
@@ -675,18 +653,17 @@ hipError_t launch_half(const FwdArgs& a) {
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
   p.drop = a.drop;
   p.diag = a.causal ? 0 : (int)a.N;
+  const FwdShape sh = fwd_shape(p.bh_count, a.N, a.causal != 0);
+  p.n_qtiles = sh.n_qtiles;
   auto go = [&](auto ks) {
     constexpr int KS = decltype(ks)::value;
-    constexpr int BM = 256 / KS;
-    p.n_qtiles = (int)((a.N + BM - 1) / BM);
-    const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.bh_count));
+    const dim3 grid((unsigned)sh.grid);
     if (a.drop.thr != 0)
       hipLaunchKernelGGL((fwd_kernel<TT, D, 8, true, KS>), grid, dim3(512), 0, a.stream, p);
     else
       hipLaunchKernelGGL((fwd_kernel<TT, D, 8, false, KS>), grid, dim3(512), 0, a.stream, p);
   };
-  const int64_t tiles = ((a.N + 255) / 256) * a.B * a.H;  // 256-row workgroups
-  if (tiles > (a.causal ? kMaxSplitCausal : kMaxSplitFull)) go(std::integral_constant<int, 1>{});
+  if (sh.ks == 1) go(std::integral_constant<int, 1>{});
   else go(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }

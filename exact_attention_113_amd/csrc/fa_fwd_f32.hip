@@ -38,9 +38,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 31, hi = lane >> 5;
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / n_qtiles;
-  const int qt = n_qtiles - 1 - (logical % n_qtiles);
+  int qt, bh;
+  f32_tile_of(blockIdx.x, gridDim.x, n_qtiles, qt, bh);
   const int q0 = qt * kBM;
   const size_t head = (size_t)bh * (size_t)N * D;
   const float* Qh = Q + head;

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_sched.h"
 
 namespace fa {
 
@@ -85,21 +86,7 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
-// How the cache is cut into chunks (one workgroup per sequence, K/V head and
-// chunk) and where the per-chunk partial results go in the workspace.
-#ifndef FA_DECODE_TARGET_WGS
-#define FA_DECODE_TARGET_WGS 4096
-#endif
-constexpr int64_t kDecodeTargetWgs = FA_DECODE_TARGET_WGS;
-constexpr int64_t kMaxSplits = 64;
-struct DecodePlan {
-  int n_splits, chunk;
-  size_t part_o_off, part_o_bytes;      // fp32 [B, H, s_q, n_splits, D]
-  size_t part_lse_off, part_lse_bytes;  // fp32 [B, H, s_q, n_splits]
-  size_t total;                         // 0 when the cache is one chunk
-};
-bool decode_plan(int64_t B, int64_t s_q, int64_t H, int64_t H_kv, int64_t max_len, int64_t D,
-                 DecodePlan* plan);
+// The chunk plan of a decode call (DecodePlan, decode_plan) is in fa_sched.h.
 
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);

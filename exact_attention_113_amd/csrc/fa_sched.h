@@ -1,0 +1,218 @@
+// Work orders of the kernels' grids: which (sequence, head, tile) each
+// workgroup takes, how many workgroups a launch has, and how the decode
+// kernel cuts a cache into chunks. Host and device code share these
+// functions, so the mapping the kernels run is the one the CPU-side
+// coverage check enumerates (every row produced exactly once, every index
+// inside its tensor).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Map a linear workgroup id to a logical one so that runs of consecutive
+// logical ids land on one XCD. Workgroups are dealt to the 8 XCDs round
+// robin by linear id; when the grid is a multiple of 8, logical id
+// (x * total/8 + s) is given to the s-th workgroup of XCD x.
+__host__ __device__ inline int xcd_logical_id(int lin, int total) {
+  if ((total & 7) != 0) return lin;
+  return (lin & 7) * (total >> 3) + (lin >> 3);
+}
+
+// Rows [s0, s0 + n) of a packed batch are sequence b: its offsets clamped
+// into [0, total] and its length to seqlen (the longest sequence the grid
+// was sized for), so malformed offsets cannot move an access out of bounds.
+__host__ __device__ inline void seq_span(const int32_t* cu, int b, int total, int seqlen, int& s0,
+                                         int& n) {
+  const int a0 = cu[b], a1 = cu[b + 1];
+  s0 = a0 < 0 ? 0 : (a0 > total ? total : a0);
+  const int s1 = a1 < s0 ? s0 : (a1 > total ? total : a1);
+  n = s1 - s0 < seqlen ? s1 - s0 : seqlen;
+}
+
+// ---- forward (bf16 / fp16) -------------------------------------------------
+
+// Workgroup lin of the forward: query tile qt (counted from the last) of
+// (sequence, head) pair p. Heavier causal query tiles come first (longest
+// job first over the CUs; in packed batches round r takes each sequence's
+// r-th tile from its end). The pairs are numbered head-major,
+// p = h * batch + b; when they divide evenly over the 8 XCDs, each XCD keeps
+// one contiguous range of p: the same heads of every sequence.
+__host__ __device__ inline void fwd_tile_of(int lin, int n_qtiles, int bh_count, int& qt, int& p) {
+  if ((bh_count & 7) == 0) {
+    const int hpx = bh_count >> 3;
+    const int xcd = lin & 7, slot = lin >> 3;
+    qt = n_qtiles - 1 - slot / hpx;
+    p = xcd * hpx + slot % hpx;
+  } else {
+    qt = n_qtiles - 1 - lin / bh_count;
+    p = lin % bh_count;
+  }
+}
+
+// A packed batch counts a sequence's tiles back from its own last one, so
+// that the slots past the end of shorter sequences come last in the
+// dispatch order; negative means no tile (the workgroup exits).
+__host__ __device__ inline int fwd_seq_tile(int qt, int n_qtiles, int n, int bm, bool packed) {
+  return packed ? qt - (n_qtiles - (n + bm - 1) / bm) : qt;
+}
+
+// Largest grids (in 256-row workgroups) whose forward splits each row
+// group's keys between two waves: causal attention up to one round of the
+// CUs, full attention up to half of one (see the forward kernel).
+constexpr int64_t kMaxSplitCausal = 256;
+constexpr int64_t kMaxSplitFull = 128;
+
+struct FwdShape {
+  int ks;        // 1: whole key ranges per wave; 2: two waves per row group
+  int bm;        // query rows per workgroup (256 / ks)
+  int n_qtiles;  // query tiles per (sequence, head)
+  int64_t grid;  // workgroups
+};
+
+// Grid of the half-precision forward for bh_count (sequence, head) pairs of
+// (at most) n rows.
+inline FwdShape fwd_shape(int64_t bh_count, int64_t n, bool causal) {
+  const int64_t tiles = ((n + 255) / 256) * bh_count;
+  FwdShape s;
+  s.ks = tiles > (causal ? kMaxSplitCausal : kMaxSplitFull) ? 1 : 2;
+  s.bm = 256 / s.ks;
+  s.n_qtiles = (int)((n + s.bm - 1) / s.bm);
+  s.grid = (int64_t)s.n_qtiles * bh_count;
+  return s;
+}
+
+// fp32 forward: workgroup lin takes query tile qt (heaviest first) of the
+// (batch, head) pair bh, each XCD a contiguous range of logical ids.
+__host__ __device__ inline void f32_tile_of(int lin, int grid, int n_qtiles, int& qt, int& bh) {
+  const int logical = xcd_logical_id(lin, grid);
+  bh = logical / n_qtiles;
+  qt = n_qtiles - 1 - logical % n_qtiles;
+}
+
+// ---- backward ---------------------------------------------------------------
+
+// Workgroup blk of either backward kernel: unit (a (sequence, head) pair,
+// numbered head-major, heads pinned to XCDs) and slot. Unit-major (the
+// default): each XCD runs one unit's tiles after another, sharing that
+// unit's operands in its L2. Round-major (small causal grids): round r takes
+// slot r of every unit, which spreads heavy and light tiles evenly over the
+// CUs.
+__host__ __device__ inline void bwd_unit_slot(int blk, int grid, bool round_major, int units,
+                                              int n_tiles, int& unit, int& slot) {
+  if (round_major) {
+    if ((units & 7) == 0) {
+      const int per_xcd = units >> 3;
+      const int s = blk >> 3;
+      unit = (blk & 7) * per_xcd + s % per_xcd;
+      slot = s / per_xcd;
+    } else {
+      unit = blk % units;
+      slot = blk / units;
+    }
+  } else {
+    const int logical = xcd_logical_id(blk, grid);
+    unit = logical / n_tiles;
+    slot = logical % n_tiles;
+  }
+}
+
+// dQ: the query tile of a slot, or -1 past the end of a shorter sequence.
+// Unit-major counts from the longest sequence's end, round-major from this
+// sequence's own end.
+__host__ __device__ inline int bwd_dq_tile(int slot, bool round_major, int n_tiles, int n, int bm) {
+  const int qt = (round_major ? (n + bm - 1) / bm : n_tiles) - 1 - slot;
+  return (qt < 0 || qt * bm >= n) ? -1 : qt;
+}
+
+constexpr int kBwdKeyTile = 128;    // keys per dK/dV workgroup
+constexpr int kBwdQueryTile = 256;  // query rows per dQ workgroup
+// Causal dQ grids of at most two workgroups per CU run round-major
+// (measured at B1 H32 N4096 D128, 512 workgroups: backward 569 against
+// 626-634 us unit-major; at 2048 workgroups and in the packed GQA batch
+// unit-major was 1.5 % and 5 % faster). Full attention's tiles all cost
+// the same, so there the order could only change the L2 sharing.
+constexpr int64_t kMaxRoundMajorDq = 512;
+// Causal dK/dV grids of at most four workgroups per CU run round-major.
+constexpr int64_t kMaxRoundMajorDkdv = 1024;
+
+struct BwdShape {
+  int n_ktiles, n_qtiles;      // key tiles (dK/dV) and query tiles (dQ) per unit
+  int64_t grid_dkdv, grid_dq;  // workgroups
+  bool rm_dkdv, rm_dq;         // round-major work orders
+};
+
+// Grids of the two backward kernels for `batch` sequences of (at most) n
+// rows, h query heads over hkv K/V heads.
+inline BwdShape bwd_shape(int64_t batch, int64_t h, int64_t hkv, int64_t n, bool causal) {
+  BwdShape s;
+  s.n_ktiles = (int)((n + kBwdKeyTile - 1) / kBwdKeyTile);
+  s.n_qtiles = (int)((n + kBwdQueryTile - 1) / kBwdQueryTile);
+  s.grid_dkdv = (int64_t)s.n_ktiles * batch * hkv;
+  s.grid_dq = (int64_t)s.n_qtiles * batch * h;
+  s.rm_dkdv = causal && s.grid_dkdv <= kMaxRoundMajorDkdv;
+  s.rm_dq = causal && s.grid_dq <= kMaxRoundMajorDq;
+  return s;
+}
+
+// ---- decode ------------------------------------------------------------------
+
+// Workgroup blk of the decode kernel: sequence b, K/V head hk, chunk split.
+__host__ __device__ inline void decode_unit(int blk, int n_splits, int hkv, int& b, int& hk,
+                                            int& split) {
+  split = blk % n_splits;
+  const int rest = blk / n_splits;
+  hk = rest % hkv;
+  b = rest / hkv;
+}
+
+// Workgroups the chunk plan aims for, and the most chunks per row (one
+// lane of the merge kernel's wave each).
+#ifndef FA_DECODE_TARGET_WGS
+#define FA_DECODE_TARGET_WGS 4096
+#endif
+constexpr int64_t kDecodeTargetWgs = FA_DECODE_TARGET_WGS;
+constexpr int64_t kMaxSplits = 64;
+
+// How the cache is cut into chunks (one workgroup per sequence, K/V head and
+// chunk) and where the per-chunk partial results go in the workspace.
+struct DecodePlan {
+  int n_splits, chunk;
+  size_t part_o_off, part_o_bytes;      // fp32 [B, H, s_q, n_splits, D]
+  size_t part_lse_off, part_lse_bytes;  // fp32 [B, H, s_q, n_splits]
+  size_t total;                         // 0 when the cache is one chunk
+};
+
+inline bool decode_plan(int64_t B, int64_t s_q, int64_t H, int64_t H_kv, int64_t max_len,
+                        int64_t D, DecodePlan* plan) {
+  if (B < 1 || s_q < 1 || H < 1 || H_kv < 1 || max_len < 0 || D < 1) return false;
+  // Enough workgroups to fill the chip a few times over, chunks of at least
+  // 128 keys (one block per wave), at most kMaxSplits chunks per row.
+  const int64_t units = B * H_kv;
+  const int64_t want = (kDecodeTargetWgs + units - 1) / units;
+  const int64_t most = max_len > 0 ? (max_len + 127) / 128 : 1;
+  int64_t n = want < most ? want : most;
+  if (n > kMaxSplits) n = kMaxSplits;
+  if (n < 1) n = 1;
+  int64_t chunk = max_len > 0 ? (max_len + n - 1) / n : 128;
+  chunk = (chunk + 127) / 128 * 128;
+  n = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
+  plan->n_splits = (int)n;
+  plan->chunk = (int)chunk;
+  auto pad = [](size_t x) { return (x + 255) / 256 * 256; };
+  if (n > 1) {
+    const size_t rows = (size_t)B * H * s_q;
+    plan->part_o_off = 0;
+    plan->part_o_bytes = pad(rows * n * D * 4);
+    plan->part_lse_off = plan->part_o_bytes;
+    plan->part_lse_bytes = pad(rows * n * 4);
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes;
+  } else {
+    plan->part_o_off = plan->part_o_bytes = plan->part_lse_off = plan->part_lse_bytes = 0;
+    plan->total = 0;
+  }
+  return true;
+}
+
+}  // namespace fa
