@@ -422,8 +422,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
         if constexpr (DROP) {
           // dS = P (keep * dP / (1 - p) - delta), the keep bit in P's sign
           // (a dropped P of 0 reads as kept, which changes nothing since
-          // its dS is 0). Written with float operations: the same steps on
-          // the integer bit pattern were compiled to wrong results.
+          // its dS is 0). Float operations on the element: this compiler
+          // evaluates __builtin_bit_cast of a vector element (p4[e]) as a
+          // bit_cast of element 0, which is what made an integer decode of
+          // the sign wrong.
           const float pv = fabsf(p4[e]);
           const float g = p4[e] < 0.f ? 0.f : dp[4 * m + e] * drop.inv_keep;
           ds[4 * m + e] = pv * (g - d4[e]);

@@ -61,8 +61,9 @@ struct F16 {
     r[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, r);
   }
-  // Scalar half extraction (a bit_cast of a vector element to a 2 x half
-  // vector was folded to the first element by the compiler).
+  // Scalar half extraction from a scalar word: this compiler evaluates
+  // __builtin_bit_cast of a vector element (v[i]) as a bit_cast of element
+  // 0, so callers pass the word itself, never a vector element.
   static __device__ __forceinline__ float lo(uint32_t x) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
   }
