@@ -83,6 +83,32 @@ inline FwdShape fwd_shape(int64_t bh_count, int64_t n, bool causal) {
   return s;
 }
 
+// fp32 forward. Unsplit (ks = 1), four waves of 32 query rows each run over
+// whole key ranges. Grids of at most kMaxSplitF32 such 128-row tiles split
+// each row group's keys over ks waves, eight waves per workgroup: ks = 4
+// (two row groups) at head dim 64, ks = 2 (four) at 128, which keeps the
+// double-buffered K/V tiles of 32 keys per split within the LDS.
+constexpr int64_t kMaxSplitF32 = 256;
+__host__ __device__ constexpr int f32_row_groups(int ks) { return ks == 1 ? 4 : 8 / ks; }
+__host__ __device__ constexpr int f32_split(int d) { return d == 64 ? 4 : 2; }
+
+struct F32Shape {
+  int ks;        // waves per row group
+  int bm;        // query rows per workgroup (32 per row group)
+  int n_qtiles;  // query tiles per (batch, head)
+  int64_t grid;  // workgroups
+};
+
+inline F32Shape f32_shape(int64_t bh_count, int64_t n, int d) {
+  F32Shape s;
+  const int64_t tiles = ((n + 127) / 128) * bh_count;
+  s.ks = tiles > kMaxSplitF32 ? 1 : f32_split(d);
+  s.bm = 32 * f32_row_groups(s.ks);
+  s.n_qtiles = (int)((n + s.bm - 1) / s.bm);
+  s.grid = (int64_t)s.n_qtiles * bh_count;
+  return s;
+}
+
 // fp32 forward: workgroup lin takes query tile qt (heaviest first) of the
 // (batch, head) pair bh, each XCD a contiguous range of logical ids.
 __host__ __device__ inline void f32_tile_of(int lin, int grid, int n_qtiles, int& qt, int& bh) {

@@ -187,12 +187,12 @@ void check_malformed(const std::string& name, const std::vector<int32_t>& cu, in
 }
 
 // fp32 forward (dense only).
-void check_forward_f32(const std::string& name, int B, int H, int N) {
+void check_forward_f32(const std::string& name, int B, int H, int N, int D) {
   ++g_cases;
   const Batch x = dense(B, N);
-  constexpr int BM = 128;
-  const int n_qtiles = (N + BM - 1) / BM;
-  const int grid = n_qtiles * B * H;
+  const fa::F32Shape sh = fa::f32_shape((int64_t)B * H, N, D);
+  const int BM = sh.bm, n_qtiles = sh.n_qtiles, grid = (int)sh.grid;
+  CHECK(BM == 32 * fa::f32_row_groups(sh.ks), "rows per workgroup %d, ks %d", BM, sh.ks);
   std::vector<int> cover(rows_of(x, H), 0);
   for (int lin = 0; lin < grid; ++lin) {
     int qt, bh;
@@ -202,7 +202,7 @@ void check_forward_f32(const std::string& name, int B, int H, int N) {
   }
   std::string why;
   CHECK(exactly_once(x, H, cover, why), "%s", why.c_str());
-  std::printf("ok %s: %d workgroups\n", name.c_str(), grid);
+  std::printf("ok %s: %d workgroups, ks %d\n", name.c_str(), grid, sh.ks);
 }
 
 // Backward: dK/dV over key tiles of each (sequence, K/V head), dQ over query
@@ -355,9 +355,14 @@ int main() {
     check_malformed("malformed offsets C", {10, 2, 2000}, 512, 8, 1, causal);
   }
   // fp32 forward.
-  check_forward_f32("fwd f32 B1 H2 N256", 1, 2, 256);
-  check_forward_f32("fwd f32 B2 H3 N1000", 2, 3, 1000);
-  check_forward_f32("fwd f32 B2 H4 N77", 2, 4, 77);
+  for (int d : {64, 128}) {
+    const std::string dd = " D" + std::to_string(d);
+    check_forward_f32("fwd f32 B1 H2 N256" + dd, 1, 2, 256, d);
+    check_forward_f32("fwd f32 B2 H3 N1000" + dd, 2, 3, 1000, d);
+    check_forward_f32("fwd f32 B2 H4 N77" + dd, 2, 4, 77, d);
+    check_forward_f32("fwd f32 B1 H16 N4096" + dd, 1, 16, 4096, d);
+    check_forward_f32("fwd f32 B3 H5 N2049" + dd, 3, 5, 2049, d);
+  }
   // Dense backward: the training shape, the round-major thresholds (dQ 512,
   // dK/dV 1024 workgroups), unit counts not a multiple of 8, ragged lengths.
   for (bool causal : {true, false}) {

@@ -44,6 +44,22 @@ def test_fp32_b1h2_n256_d64():
     check(w.name, q, k, v, w.causal, w.scale, w.dtype, all_heads(w.B, w.H), strict=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 1500), (1, 16, 2176)], ids=["split", "unsplit"])
+def test_fp32_both_grids(shape, causal, D):
+    """fp32 grids of a few query tiles split each row group's keys over
+    several waves and merge their states; grids of more than one 128-row
+    tile per CU run one wave per row group. Both with a ragged last tile,
+    every head against the oracle."""
+    B, H, N = shape
+    q, k, v = workloads.make_random((B, H, N, D), seed=17 + N + D, dtype="fp32", device=DEV)
+    o, lse = run(q, k, v, causal, D ** -0.5)
+    compare_heads(f"fp32 {shape} D{D} causal={causal}", (q, k, v),
+                  forward_oracle(D ** -0.5, causal), [("O", o, 0)], "fp32", all_heads(B, H),
+                  lse=(lse, 1), strict=True)
+
+
 def test_bf16_b2h8_n512_d64():
     w = workloads.bf16_short()
     q, k, v = workloads.make_inputs(w, device=DEV)

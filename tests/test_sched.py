@@ -54,6 +54,7 @@ MUTANTS = {
     "decode_chunk_round": ("chunk = (chunk + 127) / 128 * 128;", "chunk = chunk / 128 * 128;"),
     "split_threshold": ("s.ks = tiles > (causal ? kMaxSplitCausal : kMaxSplitFull) ? 1 : 2;\n  s.bm = 256 / s.ks;",
                         "s.ks = tiles > (causal ? kMaxSplitCausal : kMaxSplitFull) ? 1 : 2;\n  s.bm = 256;"),
+    "f32_split_rows": ("s.bm = 32 * f32_row_groups(s.ks);", "s.bm = 32 * f32_row_groups(1);"),
 }
 
 
