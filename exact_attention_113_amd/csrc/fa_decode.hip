@@ -375,6 +375,285 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecParams 
   }
 }
 
+// Decode with at most 16 query rows per (sequence, K/V head): the rows are
+// the N side of 16x16x32 MFMAs (S^T = K Q^T and O^T = V^T P^T as above),
+// which halves the accumulator, the Q fragments and the per-block softmax
+// of the 32-row tile. V is loaded into registers like K and copied to a
+// per-wave LDS stage just before its transposed reads, so that both of a
+// block's tensors are held in registers while in flight: a wave refills a
+// block's registers as soon as its scores are computed and its V is
+// staged, which keeps two blocks in flight during the rest of the step
+// (the 32-row kernel has room for one). All loads are ordinary ones whose
+// completion the compiler tracks.
+//
+// Layouts (lane l, q = l % 16, row group g = l / 16 of the wave):
+//  - score MFMA: A = K rows key0 + 16 t + q, B = Q row q; the head dim is
+//    split as d = (D/4) g + 8 s + e for k-step s and element e, the same for
+//    K and Q, so each lane reads one contiguous quarter row. The result
+//    gives lane l the scores of query q against keys key0 + 16 t + 4 g + r.
+//  - P V MFMA: B = P^T with lane l holding keys key0 + 4 g + r (elements
+//    0..3) and key0 + 16 + 4 g + r (elements 4..7), which is exactly what
+//    the score MFMAs left in the lane; A = V^T read transposed from the
+//    stage with the same key order; the result gives lane l the output
+//    elements d = 16 i + 4 g + r of query q.
+template <typename TT, int D>
+__global__ __launch_bounds__(kDecThreads, 2) void decode16_kernel(const DecParams prm) {
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int ROWB = 2 * D;      // bytes per row
+  constexpr int KS = D / 32;       // k-steps of a score MFMA
+  constexpr int DT = D / 16;       // 16-element tiles of the head dim
+  constexpr int QW = D / 4;        // head-dim elements per row group in the score MFMA
+  constexpr int RPL = 64 / CH;     // V rows per wave-wide load
+  constexpr int VL = kDKB / RPL;   // V loads per lane and block
+  constexpr int STAGE = kDKB * ROWB;
+  constexpr int OC = D / 4;        // 16-byte chunks of an fp32 output row
+  static_assert(16 * D * 4 <= STAGE, "merge slab exceeds a wave's stage");
+  __shared__ __attribute__((aligned(1024))) char vst[kDecWaves * STAGE];
+  __shared__ float stat_m[kDecWaves][16];
+  __shared__ float stat_l[kDecWaves][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 15, g = lane >> 4;
+
+  int b, hk, split;
+  decode_unit(blockIdx.x, prm.n_splits, prm.hkv, b, hk, split);
+  const int L = min(max(prm.seqlens[b], 0), prm.max_len);
+  const int k_lo = split * prm.chunk;
+  const int k_hi = min(L, k_lo + prm.chunk);
+  const int nblk = k_hi > k_lo ? (k_hi - k_lo + kDKB - 1) / kDKB : 0;
+  const int rows = prm.group * prm.s_q;
+
+  // Query row q: head hk * group + q / s_q, new token q % s_q; it sees the
+  // keys [k_lo, lim) of the chunk.
+  const int gq = q / prm.s_q, tq = q - gq * prm.s_q;
+  const bool row_ok = q < rows;
+  const int lim = min(min(L, L - prm.s_q + tq + 1), k_hi);
+
+  const size_t kv_stride = (size_t)prm.hkv * D;
+  const uint16_t* Kb = prm.k + ((size_t)b * prm.cap * prm.hkv + hk) * D;
+  const uint16_t* Vb = prm.v + ((size_t)b * prm.cap * prm.hkv + hk) * D;
+  // Rows past the cache read its last row (their scores are masked); the
+  // capacity is at least one row.
+  const int last = max(L - 1, 0);
+  char* stage = vst + w * STAGE;
+  auto swz = [](int r) __attribute__((always_inline)) {
+    return CH == 16 ? 4 * (r & 3) : 2 * (r & 3);
+  };
+
+  struct Blk {
+    u32x4 k[2][KS];
+    u32x4 v[VL];
+  };
+  auto load_block = [&](int j, Blk& x) __attribute__((always_inline)) {
+    const int key0 = k_lo + kDKB * j;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* kr = Kb + (size_t)min(key0 + 16 * t + q, last) * kv_stride + QW * g;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) x.k[t][st] = *(const u32x4*)(kr + 8 * st);
+    }
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int r = RPL * i + lane / CH, c = lane % CH;
+      x.v[i] = *(const u32x4*)(Vb + (size_t)min(key0 + r, last) * kv_stride + 8 * c);
+    }
+  };
+
+  u32x4 qf[KS];
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY;  // running maximum of query q, log2 units
+  float lsum = 0.f;        // this lane's share of the running sum
+
+  // Transposed-read address of row group g, lane x = l % 16: row 4 g + x / 4
+  // (the second read 16 rows further), head-dim elements 4 (x % 4) .. + 3 of
+  // tile i, i.e. 16-byte chunk 2 i + (x % 4) / 2 at byte 8 (x % 2).
+  const int trow = 4 * g + ((lane & 15) >> 2);
+  const int tcol = ((lane & 15) >> 1) & 1;
+  const uint32_t tbase = (uint32_t)(uintptr_t)(lds_void*)(stage + trow * ROWB + 8 * (lane & 1));
+
+  // One block: stage V, scores, refill the block's registers (when `next`
+  // names a block), masked online softmax, P V.
+  auto compute_block = [&](int j, Blk& x, int next) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int r = RPL * i + lane / CH, c = lane % CH;
+      *(u32x4*)(stage + r * ROWB + 16 * (c ^ swz(r))) = x.v[i];
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) s[t] = TT::mma16(x.k[t][st], qf[st], s[t]);
+    }
+    if (next >= 0) load_block(next, x);
+    const int key0 = k_lo + kDKB * j;
+    uint32_t okm = 0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = key0 + 16 * t + 4 * g + r < lim;
+        okm |= ok ? (1u << (4 * t + r)) : 0u;
+        mx = ok ? fmaxf(mx, s[t][r]) : mx;
+      }
+    mx = quad_max(mx);
+    const float tmx = mx == -INFINITY ? -INFINITY : mx * prm.c;
+    const float mnew = fmaxf(mrun, tmx);
+    // Nothing visible yet: keep alpha = 1 (the state is still empty).
+    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
+    const float nm = -mnew;
+    float p[8];
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = fast_exp2(fmaf(s[t][r], prm.c, nm));
+        p[4 * t + r] = ((okm >> (4 * t + r)) & 1u) ? e : 0.f;
+        sum += p[4 * t + r];
+      }
+    lsum = fmaf(lsum, alpha, sum);
+    mrun = mnew;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+    }
+    const u32x4 pf = {TT::pack2(p[0], p[1]), TT::pack2(p[2], p[3]), TT::pack2(p[4], p[5]),
+                      TT::pack2(p[6], p[7])};
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      const uint32_t a = tbase + 16 * ((2 * i + tcol) ^ swz(trow));
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(a + 16 * ROWB));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), u2 = __builtin_bit_cast(u32x2, up);
+      const u32x4 va = {l2[0], l2[1], u2[0], u2[1]};
+      oacc[i] = TT::mma16(va, pf, oacc[i]);
+    }
+  };
+
+  // This wave's blocks w, w + 4, ...: block i in register set i % 2. Both
+  // first blocks are issued at once, then Q (after them: the compiler's wait
+  // for Q covers both, so Q adds no round trip of its own); each block's
+  // set is refilled with the block two further on while that block is
+  // computed.
+  const int ni = nblk > w ? (nblk - w + kDecWaves - 1) / kDecWaves : 0;
+  if (ni > 0) {
+    Blk A, B;
+    load_block(w, A);
+    load_block(w + kDecWaves, B);
+    asm volatile("" ::: "memory");
+    {
+      const int qc = row_ok ? q : 0;
+      const int gqc = qc / prm.s_q, tqc = qc - gqc * prm.s_q;
+      const uint16_t* qrow =
+          prm.q + ((size_t)(b * prm.s_q + tqc) * prm.heads + hk * prm.group + gqc) * D + QW * g;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) qf[st] = *(const u32x4*)(qrow + 8 * st);
+      const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) qf[st] = (qf[st] ^ prm.qsign) & qmask;
+    }
+    // Inside the loop both sets are always refilled, so the loads in flight
+    // at its head are the same on every pass and the compiler's waits stay
+    // exact; the last two or three blocks follow it.
+    int i = 0;
+    for (; i + 3 < ni; i += 2) {
+      compute_block(w + kDecWaves * i, A, w + kDecWaves * (i + 2));
+      compute_block(w + kDecWaves * (i + 1), B, w + kDecWaves * (i + 3));
+    }
+    if (i + 2 < ni) {
+      compute_block(w + kDecWaves * i, A, w + kDecWaves * (i + 2));
+      compute_block(w + kDecWaves * (i + 1), B, -1);
+      compute_block(w + kDecWaves * (i + 2), A, -1);
+    } else {
+      compute_block(w + kDecWaves * i, A, -1);
+      if (i + 1 < ni) compute_block(w + kDecWaves * (i + 1), B, -1);
+    }
+  }
+
+  // Merge the four waves' states as in the 32-row kernel; each wave's
+  // weighted accumulator goes to its own stage (16 fp32 rows).
+  const float lrow = quad_sum(lsum);
+  if (g == 0) {
+    stat_m[w][q] = mrun;
+    stat_l[w][q] = lrow;
+  }
+  __syncthreads();
+  auto row_stats = [&](int row, float& M, float& Ltot) __attribute__((always_inline)) {
+    M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x) M = fmaxf(M, stat_m[x][row]);
+    Ltot = 0.f;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x)
+      Ltot += stat_m[x][row] == -INFINITY ? 0.f : fast_exp2(stat_m[x][row] - M) * stat_l[x][row];
+  };
+  {
+    float M, Ltot;
+    row_stats(q, M, Ltot);
+    const float f = mrun == -INFINITY ? 0.f : fast_exp2(mrun - M);
+    // Row q of the slab, 16-byte chunk c stored at c ^ (q % OC).
+    float* ob = (float*)stage + (size_t)q * D;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) *(f32x4*)(ob + 4 * ((4 * i + g) ^ (q % OC))) = oacc[i] * f;
+  }
+  __syncthreads();
+  {
+    constexpr int SEG = D / 16;  // output elements per thread
+    const int row = tid >> 4, d0 = (tid & 15) * SEG;
+    if (row < rows) {
+      float M, Ltot;
+      row_stats(row, M, Ltot);
+      const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+      float acc[SEG];
+#pragma unroll
+      for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int x = 0; x < kDecWaves; ++x) {
+        const float* src = (const float*)(vst + x * STAGE) + (size_t)row * D;
+#pragma unroll
+        for (int e = 0; e < SEG; e += 4) {
+          const f32x4 y = *(const f32x4*)(src + 4 * (((d0 + e) / 4) ^ (row % OC)));
+          acc[e] += y[0];
+          acc[e + 1] += y[1];
+          acc[e + 2] += y[2];
+          acc[e + 3] += y[3];
+        }
+      }
+      const int rg = row / prm.s_q, rt = row - rg * prm.s_q;
+      const int rh = hk * prm.group + rg;
+      const float lse_row = Ltot > 0.f ? kLn2 * (M + __log2f(Ltot)) : -INFINITY;
+      if (prm.n_splits == 1) {
+        uint16_t* orow = prm.o + ((size_t)(b * prm.s_q + rt) * prm.heads + rh) * D + d0;
+        if constexpr (SEG == 8) {
+          u32x4 out;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) out[u] = TT::pack2(acc[2 * u] * inv, acc[2 * u + 1] * inv);
+          *(u32x4*)orow = out;
+        } else {
+          u32x2 out;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) out[u] = TT::pack2(acc[2 * u] * inv, acc[2 * u + 1] * inv);
+          *(u32x2*)orow = out;
+        }
+        if ((tid & 15) == 0) prm.lse[((size_t)b * prm.heads + rh) * prm.s_q + rt] = lse_row;
+      } else {
+        const size_t prow = ((size_t)(b * prm.heads + rh) * prm.s_q + rt) * prm.n_splits + split;
+        float* po = prm.part_o + prow * D + d0;
+#pragma unroll
+        for (int e = 0; e < SEG; e += 4)
+          *(f32x4*)(po + e) = f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+        if ((tid & 15) == 0) prm.part_lse[prow] = lse_row;
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -463,8 +742,12 @@ hipError_t launch_typed(const DecodeArgs& a, const DecodePlan& plan) {
   p.c = fabsf(a.scale) * kLog2e;
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const int64_t grid = a.B * a.H_kv * plan.n_splits;
-  hipLaunchKernelGGL((decode_kernel<TT, D>), dim3((unsigned)grid), dim3(kDecThreads), 0, a.stream,
-                     p);
+  if (p.group * p.s_q <= 16)
+    hipLaunchKernelGGL((decode16_kernel<TT, D>), dim3((unsigned)grid), dim3(kDecThreads), 0,
+                       a.stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<TT, D>), dim3((unsigned)grid), dim3(kDecThreads), 0,
+                       a.stream, p);
   if (plan.n_splits > 1) {
     const int n_rows = (int)(a.B * a.H * a.s_q);
     hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((unsigned)((n_rows + 3) / 4)), dim3(256),

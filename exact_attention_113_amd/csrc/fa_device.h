@@ -37,6 +37,10 @@ struct Bf16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     bf16x2 r;
     r[0] = (__bf16)lo;
@@ -53,6 +57,10 @@ struct Bf16 {
 struct F16 {
   static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -85,6 +93,23 @@ __device__ __forceinline__ float half_swap_max(float v) {
 
 __device__ __forceinline__ float half_swap_sum(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Combine over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48): the 32-lane swap above, then v_permlane16_swap, which exchanges
+// rows 0 <-> 1 and 2 <-> 3 between its operands the same way.
+__device__ __forceinline__ float quad_max(float v) {
+  v = half_swap_max(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v = half_swap_sum(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
                                             __builtin_bit_cast(uint32_t, v), false, false);
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }

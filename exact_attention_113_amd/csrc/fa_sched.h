@@ -185,12 +185,14 @@ inline BwdShape bwd_shape(int64_t batch, int64_t h, int64_t hkv, int64_t n, bool
 // ---- decode ------------------------------------------------------------------
 
 // Workgroup blk of the decode kernel: sequence b, K/V head hk, chunk split.
+// Heads vary fastest: the workgroups dispatched together read the pieces of
+// the same cache rows (each row holds every K/V head of one token).
 __host__ __device__ inline void decode_unit(int blk, int n_splits, int hkv, int& b, int& hk,
                                             int& split) {
-  split = blk % n_splits;
-  const int rest = blk / n_splits;
-  hk = rest % hkv;
-  b = rest / hkv;
+  hk = blk % hkv;
+  const int rest = blk / hkv;
+  split = rest % n_splits;
+  b = rest / n_splits;
 }
 
 // Workgroups the chunk plan aims for, and the most chunks per row (one

@@ -39,7 +39,7 @@ def check(name, o, lse, q, k, v, lens, scale, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("H_kv,s_q", [(8, 1), (2, 1), (1, 1), (2, 4), (1, 4)])
+@pytest.mark.parametrize("H_kv,s_q", [(8, 1), (2, 1), (1, 1), (2, 4), (1, 2), (1, 3), (1, 4)])
 def test_decode_chunked(dtype, D, H_kv, s_q):
     """Caches of length 0, 1, 3, 333 and 700 (capacity 700), cut into
     128-key chunks merged by LSE; with s_q = 4 some rows see no key."""

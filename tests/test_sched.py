@@ -50,7 +50,8 @@ MUTANTS = {
                              "unit = (blk & 7) * per_xcd + s / per_xcd;"),
     "seq_end_unclamped": ("const int s1 = a1 < s0 ? s0 : (a1 > total ? total : a1);",
                           "const int s1 = a1 < s0 ? s0 : a1;"),
-    "decode_unit_swap": ("hk = rest % hkv;\n  b = rest / hkv;", "b = rest % hkv;\n  hk = rest / hkv;"),
+    "decode_unit_swap": ("split = rest % n_splits;\n  b = rest / n_splits;",
+                         "b = rest % n_splits;\n  split = rest / n_splits;"),
     "decode_chunk_round": ("chunk = (chunk + 127) / 128 * 128;", "chunk = chunk / 128 * 128;"),
     "split_threshold": ("s.ks = tiles > (causal ? kMaxSplitCausal : kMaxSplitFull) ? 1 : 2;\n  s.bm = 256 / s.ks;",
                         "s.ks = tiles > (causal ? kMaxSplitCausal : kMaxSplitFull) ? 1 : 2;\n  s.bm = 256;"),
