@@ -63,8 +63,10 @@ namespace {
 // 63.4 against 51.2, N2048 88.1 against 73.8. (Four-wave workgroups of 128
 // rows with whole key ranges, one wave per SIMD, measured 8 % slower than
 // the split at causal N = 1024 and 15 % at B2 H8 N512 D64.)
-// (The grid rule, kMaxSplitCausal and kMaxSplitFull, is fwd_shape in fa_sched.h.)
-constexpr int kBN = 64;                 // keys per LDS tile
+// At head dim 64 the shortest grids split the keys four ways (64-row
+// workgroups, 128-key tiles). (The grid rule, kMaxSplitCausal,
+// kMaxSplitFull and kMaxSplit4, is fwd_shape in fa_sched.h.)
+constexpr int kBN = 64;                 // keys per LDS tile (whole key ranges, two splits)
 constexpr int kKB = 32;                 // keys per pipeline step
 constexpr float kTau = 8.0f;
 constexpr float kSumCap = 256.0f;       // 2^kTau
@@ -112,17 +114,19 @@ struct FwdParams {
 // in the key loop and ran 1.46x slower at N = 4096, D = 128.)
 template <typename TT, int D, int NW, bool DROP, int KS>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
-  // KS = 2 (short sequences): the waves form NW / 2 row groups of 32 rows,
-  // and the two waves of a group take alternate 32-key blocks of its keys,
-  // halving the key loop's length; their partial results are merged at the
-  // end (the same rescale-and-add as between blocks of the online softmax).
+  // KS = 2 or 4 (short sequences): the waves form NW / KS row groups of 32
+  // rows, and the KS waves of a group take every KS-th 32-key block of its
+  // keys, cutting the key loop's length KS-fold; their partial results are
+  // merged at the end (the same rescale-and-add as between blocks of the
+  // online softmax). A K/V tile then holds one block per split.
   constexpr int NRG = NW / KS;                // row groups of 32 query rows
   constexpr int kBM = 32 * NRG;               // query rows per workgroup
+  constexpr int BN = KS == 4 ? 128 : kBN;     // keys per LDS tile
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                 // bytes per row
-  constexpr int TILEB = kBN * ROWB;           // bytes per K or V tile
+  constexpr int TILEB = BN * ROWB;            // bytes per K or V tile
   constexpr int RPI = 64 / CH;                // rows per wave-wide direct load (1 KiB)
-  constexpr int LPW = kBN / (NW * RPI);       // direct loads per wave, tile and tensor
+  constexpr int LPW = BN / (NW * RPI);        // direct loads per wave, tile and tensor
   constexpr int DB = D / 32;                  // 32-row blocks of the head dim
   constexpr int KK = D / 16;                  // k-steps of the score MFMA
   static_assert(LPW >= 1, "tile too small for one direct load per wave");
@@ -140,12 +144,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   __shared__ __attribute__((aligned(1024))) char kb3[TILEB2];
   __shared__ __attribute__((aligned(1024))) char vb2[TILEB2];
   __shared__ __attribute__((aligned(1024))) char vb3[TILEB2];
-  __shared__ float xm[KS == 2 ? NRG : 1][64], xl[KS == 2 ? NRG : 1][64];  // merge of key halves
+  // Merge of the key splits: reference and sum share of each wave but the
+  // first of its row group.
+  constexpr int NX = KS > 1 ? NRG * (KS - 1) : 1;
+  __shared__ float xm[NX][64], xl[NX][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int lq = lane & 31, hi = lane >> 5;
-  const int rg = w % NRG, kh = w / NRG;  // row group; key half (KS = 2)
+  const int rg = w % NRG, kh = w / NRG;  // row group; key split (KS > 1)
 
   const float c = prm.c;
   const uint32_t qsign = prm.qsign;
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   const int diag = prm.diag;
   const int kv_end = min(N, q0 + kBM + diag);
   const int nb = (kv_end + kKB - 1) / kKB;  // 32-key steps of the workgroup
-  const int ntile = (kv_end + kBN - 1) / kBN;
+  const int ntile = (kv_end + BN - 1) / BN;
   const int wave_end = min(N, qw0 + 32 + diag);
   // Last step this wave computes (-1: every row of the wave is past N).
   const int last_b = qw0 < N ? (wave_end - 1) / kKB : -1;
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   // (their scores are masked).
   auto load_tile = [&](const uint16_t* Xh, int t, char* dst, bool is_v)
       __attribute__((always_inline)) {
-    const int k0 = t * kBN;
+    const int k0 = t * BN;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int R0 = (w * LPW + i) * RPI;
@@ -549,14 +556,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
     }
     store_tile_rows<TT, D>(oacc, inv, stage, prm.o + qbase + (size_t)qw0 * sq, sq, N - qw0, lane);
   } else {
-    // Key halves: this wave's step j computes block 2j + kh, the kh half of
-    // K/V tile j, so one step per tile. K tile t lives in kb[t % 2] and V
-    // tile t in vb[t % 2]; step j reads K tile j + 1 and V tile j - 1, and
-    // the barrier before it sends K tile j + 2 and V tile j into the
-    // buffers step j - 1 was the last to read. K tile 2 goes out once every
-    // wave has taken block kh's scores from K tile 0.
-    const int jl = last_b >= kh ? (last_b - kh) / 2 : -1;  // this wave's last step
-    const int jmax = (nb - 1) / 2;                         // the workgroup's last block step
+    // Key splits: this wave's step j computes block KS j + kh, the kh-th
+    // 32-key block of K/V tile j, so one step per tile. K tile t lives in
+    // kb[t % 2] and V tile t in vb[t % 2]; step j reads K tile j + 1 and V
+    // tile j - 1, and the barrier before it sends K tile j + 2 and V tile j
+    // into the buffers step j - 1 was the last to read. K tile 2 goes out
+    // once every wave has taken block kh's scores from K tile 0.
+    const int jl = last_b >= kh ? (last_b - kh) / KS : -1;  // this wave's last step
+    const int jmax = (nb - 1) / KS;                         // the workgroup's last block step
     if (jl >= 0) scores(kb0, kh, sA);
     __syncthreads();
     if (ntile > 2) load_tile(Kh, 2, kb0, false);
@@ -566,7 +573,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
     }
     auto half_step = [&](int j, const char* kt, const char* vt, f32x16& cur, f32x16& nxt,
                          const u32x4(&pprev)[2], u32x4(&pcur)[2]) __attribute__((always_inline)) {
-      const int b = 2 * j + kh;
+      const int b = KS * j + kh;
       if (j <= jl) {
         if (b >= first_edge) step(True{}, True{}, b, kt, vt, cur, nxt, pprev, pcur);
         else step(False{}, True{}, b, kt, vt, cur, nxt, pprev, pcur);
@@ -590,14 +597,24 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
       }
     }
 
-    // The wave of key half 1 hands its reference maximum, sum share and
-    // accumulator to the wave of half 0 with the same rows, through the tile
-    // buffer of its row group (free once every wave is past its last P V);
-    // that wave rescales both to the larger reference, adds, and stores.
+    // The waves of splits 1 .. KS-1 hand their reference maximum, sum share
+    // and accumulator to the wave of split 0 with the same rows, each through
+    // a slot of its own in the tile buffers (free once every wave is past
+    // its last P V); that wave rescales all of them to the largest
+    // reference, adds, and stores.
     wait_vmem();
     __syncthreads();
-    float* xo = (float*)(rg == 0 ? kb0 : rg == 1 ? kb1 : rg == 2 ? vb0 : vb1);
-    if (kh == 1) {
+    constexpr int SLOTB = DB * 16 * 64 * 4;  // bytes of one wave's accumulator
+    constexpr int PERBUF = TILEB / SLOTB;    // slots per tile buffer
+    static_assert(PERBUF >= 1 && 4 * PERBUF >= NRG * (KS - 1), "merge slots exceed the buffers");
+    auto slot_ptr = [&](int sl) __attribute__((always_inline)) {
+      const int bsel = sl / PERBUF;
+      char* buf = bsel == 0 ? kb0 : bsel == 1 ? kb1 : bsel == 2 ? vb0 : vb1;
+      return (float*)(buf + (sl % PERBUF) * SLOTB);
+    };
+    if (kh > 0) {
+      const int sl = rg * (KS - 1) + kh - 1;
+      float* xo = slot_ptr(sl);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -605,32 +622,47 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
           *(f32x4*)(xo + 4 * ((db * 4 + r4) * 64 + lane)) =
               f32x4{oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2],
                     oacc[db][4 * r4 + 3]};
-      xm[rg][lane] = mref;
-      xl[rg][lane] = lsum;
+      xm[sl][lane] = mref;
+      xl[sl][lane] = lsum;
     }
     __syncthreads();
     if (kh == 0) {
-      const float m1 = xm[rg][lane], l1 = xl[rg][lane];
-      const float mm = fmaxf(mref, m1);
+      float mm = mref;
+#pragma unroll
+      for (int x = 0; x < KS - 1; ++x) mm = fmaxf(mm, xm[rg * (KS - 1) + x][lane]);
       const float a0 = mref == -INFINITY ? 0.f : fast_exp2(mref - mm);
-      const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
-      lsum = lsum * a0 + l1 * a1;
+      lsum *= a0;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 o1 = *(const f32x4*)(xo + 4 * ((db * 4 + r4) * 64 + lane));
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= a0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) oacc[db][4 * r4 + e] = oacc[db][4 * r4 + e] * a0 + o1[e] * a1;
-        }
+      for (int x = 0; x < KS - 1; ++x) {
+        const int sl = rg * (KS - 1) + x;
+        const float m1 = xm[sl][lane];
+        const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+        lsum = fmaf(xl[sl][lane], a1, lsum);
+        const float* xo = slot_ptr(sl);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 o1 = *(const f32x4*)(xo + 4 * ((db * 4 + r4) * 64 + lane));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              oacc[db][4 * r4 + e] = fmaf(o1[e], a1, oacc[db][4 * r4 + e]);
+          }
+        // One partner's accumulator at a time in registers.
+        asm volatile("" ::: "memory");
+      }
       mref = mm;
       const float ltot = half_swap_sum(lsum);
       const float inv = (DROP ? prm.drop.inv_keep : 1.f) / ltot;
       if (qi < N && hi == 0) prm.lse[lbase + qi] = kLn2 * (mref + __log2f(ltot));
-      // The wave has read all of its row group's buffer: it stages its rows
-      // there (store_tile_rows).
-      store_tile_rows<TT, D>(oacc, inv, (char*)xo, prm.o + qbase + (size_t)qw0 * sq, sq,
-                             N - qw0, lane);
+      // The wave has read all of its row group's slots: it stages its rows
+      // in the first of them (store_tile_rows).
+      store_tile_rows<TT, D>(oacc, inv, (char*)slot_ptr(rg * (KS - 1)),
+                             prm.o + qbase + (size_t)qw0 * sq, sq, N - qw0, lane);
     }
   }
 }
@@ -653,7 +685,7 @@ hipError_t launch_half(const FwdArgs& a) {
   p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
   p.drop = a.drop;
   p.diag = a.causal ? 0 : (int)a.N;
-  const FwdShape sh = fwd_shape(p.bh_count, a.N, a.causal != 0);
+  const FwdShape sh = fwd_shape(p.bh_count, a.N, a.causal != 0, D);
   p.n_qtiles = sh.n_qtiles;
   auto go = [&](auto ks) {
     constexpr int KS = decltype(ks)::value;
@@ -664,7 +696,8 @@ hipError_t launch_half(const FwdArgs& a) {
       hipLaunchKernelGGL((fwd_kernel<TT, D, 8, false, KS>), grid, dim3(512), 0, a.stream, p);
   };
   if (sh.ks == 1) go(std::integral_constant<int, 1>{});
-  else go(std::integral_constant<int, 2>{});
+  else if (sh.ks == 2 || D != 64) go(std::integral_constant<int, 2>{});
+  else if constexpr (D == 64) go(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }
 

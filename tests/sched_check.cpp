@@ -98,11 +98,11 @@ bool exactly_once(const Batch& x, int heads, const std::vector<int>& cover, std:
 }
 
 // Half-precision forward (dense or packed, grouped heads).
-void check_forward(const std::string& name, const Batch& x, int H, int Hkv, bool causal) {
+void check_forward_d(const std::string& name, const Batch& x, int H, int Hkv, bool causal, int d) {
   ++g_cases;
   const int batch = (int)x.lens.size();
   const int bh_count = batch * H;
-  const fa::FwdShape sh = fa::fwd_shape(bh_count, x.seqlen, causal);
+  const fa::FwdShape sh = fa::fwd_shape(bh_count, x.seqlen, causal, d);
   CHECK(sh.bm * sh.ks == 256 && sh.n_qtiles * sh.bm >= x.seqlen, "shape");
   CHECK(sh.grid < 0x7fffffff, "grid %lld", (long long)sh.grid);
   const int group = H / Hkv;
@@ -137,7 +137,13 @@ void check_forward(const std::string& name, const Batch& x, int H, int Hkv, bool
   }
   std::string why;
   CHECK(exactly_once(x, H, cover, why), "%s", why.c_str());
-  std::printf("ok %s: %lld workgroups, key split %d\n", name.c_str(), (long long)sh.grid, sh.ks);
+  std::printf("ok %s D%d: %lld workgroups, key split %d\n", name.c_str(), d, (long long)sh.grid,
+              sh.ks);
+}
+
+// Both head dims: their grid rules differ for the shortest grids.
+void check_forward(const std::string& name, const Batch& x, int H, int Hkv, bool causal) {
+  for (int d : {64, 128}) check_forward_d(name, x, H, Hkv, causal, d);
 }
 
 // Malformed offsets (decreasing, or past the end of the packed tensors):
@@ -147,7 +153,8 @@ void check_malformed(const std::string& name, const std::vector<int32_t>& cu, in
   ++g_cases;
   Batch x{true, std::vector<int>(cu.size() - 1, 0), cu, total, total};
   const int batch = (int)x.lens.size();
-  const fa::FwdShape sh = fa::fwd_shape(batch * H, x.seqlen, causal);
+  for (int d : {64, 128}) {
+  const fa::FwdShape sh = fa::fwd_shape(batch * H, x.seqlen, causal, d);
   for (int lin = 0; lin < (int)sh.grid; ++lin) {
     int qt, p;
     fa::fwd_tile_of(lin, sh.n_qtiles, batch * H, qt, p);
@@ -161,6 +168,7 @@ void check_malformed(const std::string& name, const std::vector<int32_t>& cu, in
       CHECK(row_of(x, Hkv, b, h / (H / Hkv), s0, i) < rows_of(x, Hkv), "K/V row out of bounds");
       CHECK(stat_of(x, H, b, h, s0, i) < rows_of(x, H), "LSE out of bounds");
     }
+  }
   }
   const fa::BwdShape bs = fa::bwd_shape(batch, H, Hkv, x.seqlen, causal);
   for (int blk = 0; blk < (int)bs.grid_dkdv; ++blk) {
