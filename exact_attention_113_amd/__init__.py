@@ -11,7 +11,8 @@ kernels; there is no fallback path.
     o, lse = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None)
 
 Tensors are contiguous [B, H, N, D] of float32, float16 or bfloat16 on the
-GPU; the default scale is 1/sqrt(D).
+GPU (k and v may have H_kv heads, H_kv dividing H: query head h reads K/V
+head h // (H // H_kv)); the default scale is 1/sqrt(D).
 """
 
 import math
@@ -31,9 +32,12 @@ def _stream_handle(t):
 
 
 def _check_qkv(q, k, v):
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError(f"q, k, v must share one [B, H, N, D] shape, got "
-                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    """Checks q [B, H, N, D] and k, v [B, H_kv, N, D] with H_kv dividing H;
+    returns H_kv."""
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or \
+            k.shape[2:] != q.shape[2:] or k.shape[1] < 1 or q.shape[1] % k.shape[1] != 0:
+        raise ValueError(f"need q [B, H, N, D] and k, v [B, H_kv, N, D] with H_kv dividing H, "
+                         f"got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError(f"dtype must be float32, float16 or bfloat16 (all equal), got "
                         f"{q.dtype}, {k.dtype}, {v.dtype}")
@@ -44,6 +48,7 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be contiguous")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
+    return k.shape[1]
 
 
 def _check_buffer(name, t, shape, dtype, device):
@@ -82,9 +87,10 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, dropout_p=0.0
     """Fused forward. Returns (o, lse): o like q, lse fp32 [B, H, N] (natural log).
 
     dropout_p > 0 drops attention probabilities with counter-based bits keyed by
-    (seed, offset); the same arguments to `backward` regenerate them.
+    (seed, offset); the same arguments to `backward` regenerate them. k and v
+    may have fewer heads than q (grouped K/V heads).
     """
-    _check_qkv(q, k, v)
+    H_kv = _check_qkv(q, k, v)
     B, H, N, D = q.shape
     if scale is None:
         scale = default_scale(D)
@@ -96,7 +102,13 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, dropout_p=0.0
     _check_buffer("lse", lse, (B, H, N), torch.float32, q.device)
     lib = _lib.load()
     with torch.cuda.device(q.device):
-        if dropout_p:
+        if H_kv != H:
+            st = lib.fa_forward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, H_kv, N, D, float(scale),
+                                    int(bool(causal)), _DTYPES[q.dtype], float(dropout_p),
+                                    int(seed), int(offset), _stream_handle(q))
+            _lib.check("fa_forward_gqa", st)
+        elif dropout_p:
             st = lib.fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                         lse.data_ptr(), B, H, N, D, float(scale),
                                         int(bool(causal)), _DTYPES[q.dtype], float(dropout_p),
@@ -219,8 +231,10 @@ def backward_workspace_bytes(B, H, N, D):
 def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, dropout_p=0.0,
              seed=0, offset=0, out=None):
     """Backward from the forward's o and lse (and its dropout arguments).
-    Returns (dq, dk, dv); `out` may give the three output tensors."""
-    _check_qkv(q, k, v)
+    Returns (dq, dk, dv), dk and dv shaped like k (with grouped K/V heads, the
+    sums over each K/V head's query heads); `out` may give the three output
+    tensors."""
+    H_kv = _check_qkv(q, k, v)
     for name, t in (("o", o), ("do", do)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must match q (shape, dtype, device, contiguous)")
@@ -238,14 +252,20 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, drop
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-            _check_buffer(name, t, q.shape, q.dtype, q.device)
+        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            _check_buffer(name, t, like.shape, q.dtype, q.device)
     lib = _lib.load()
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-            workspace.numel(), B, H, N, D, float(scale), int(bool(causal)), _DTYPES[q.dtype])
+            workspace.numel())
+    args = ptrs + (B, H, N, D, float(scale), int(bool(causal)), _DTYPES[q.dtype])
     with torch.cuda.device(q.device):
-        if dropout_p:
+        if H_kv != H:
+            st = lib.fa_backward_gqa(*ptrs, B, H, H_kv, N, D, float(scale), int(bool(causal)),
+                                     _DTYPES[q.dtype], float(dropout_p), int(seed), int(offset),
+                                     _stream_handle(q))
+            _lib.check("fa_backward_gqa", st)
+        elif dropout_p:
             st = lib.fa_backward_dropout(*args, float(dropout_p), int(seed), int(offset),
                                          _stream_handle(q))
             _lib.check("fa_backward_dropout", st)

@@ -30,6 +30,10 @@ PROTOTYPES = {
                                    _I64, _I64, _F, _I, _I, _P]),
     "fa_backward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
                                            _I64, _F, _I, _I, _P]),
+    "fa_forward_gqa": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _I,
+                                      _I, _F, _U64, _U64, _P]),
+    "fa_backward_gqa": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64,
+                                       _I64, _I64, _I64, _F, _I, _I, _F, _U64, _U64, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
 }

@@ -92,9 +92,18 @@ bool backward_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t D, BwdWo
 
 namespace {
 
+// H_kv K/V heads shared by groups of H / H_kv query heads.
+fa_status check_group(int64_t H, int64_t H_kv, const char* who) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: H_kv (%lld) must divide H (%lld)", who,
+                (long long)H_kv, (long long)H);
+  return FA_OK;
+}
+
 fa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
-                       int dtype, void* stream, const fa::DropParams& drop, const char* who) {
+                       int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, float scale,
+                       int causal, int dtype, void* stream, const fa::DropParams& drop,
+                       const char* who) {
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o and lse must be non-NULL", who);
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
@@ -102,8 +111,10 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   if (misaligned(lse, 4)) return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", who);
   fa_status s = check_shape(B, H, N, D, scale, dtype);
   if (s != FA_OK) return s;
+  s = check_group(H, H_kv, who);
+  if (s != FA_OK) return s;
   fa::FwdArgs a{q,     k,      v,     o,     lse, B, H, N, D, scale, causal, dtype, (hipStream_t)stream,
-                H,     nullptr, 0,    drop};
+                H_kv,  nullptr, 0,    drop};
   return hip_status(fa::launch_forward(a), who);
 }
 
@@ -111,8 +122,8 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
 // the workspace layout the call needs.
 fa_status check_backward(const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                         int64_t B, int64_t H, int64_t N, int64_t D, float scale, int dtype,
-                         const char* who, fa::BwdWorkspace* ws) {
+                         int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, float scale,
+                         int dtype, const char* who, fa::BwdWorkspace* ws) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return fail(FA_ERR_INVALID_ARGUMENT,
                 "%s: q, k, v, o, dout, lse, dq, dk, dv must be non-NULL", who);
@@ -122,6 +133,8 @@ fa_status check_backward(const void* q, const void* k, const void* v, const void
   if (misaligned(lse, 4)) return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", who);
   fa_status s = check_shape(B, H, N, D, scale, dtype);
   if (s != FA_OK) return s;
+  s = check_group(H, H_kv, who);
+  if (s != FA_OK) return s;
   if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: fp32 backward is not supported", who);
   if (!fa::backward_workspace_layout(B, H, N, D, ws))
     return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace size overflows", who);
@@ -130,12 +143,12 @@ fa_status check_backward(const void* q, const void* k, const void* v, const void
 
 fa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
-                        int64_t D, float scale, int causal, int dtype, void* stream,
-                        const fa::DropParams& drop, const char* who) {
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                        int64_t H_kv, int64_t N, int64_t D, float scale, int causal, int dtype,
+                        void* stream, const fa::DropParams& drop, const char* who) {
   fa::BwdWorkspace ws;
-  fa_status s = check_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, dtype, who,
-                               &ws);
+  fa_status s = check_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, D, scale, dtype,
+                               who, &ws);
   if (s != FA_OK) return s;
   if (!workspace)
     return fail(FA_ERR_WORKSPACE, "%s: workspace is NULL (needs %lld bytes)", who,
@@ -146,7 +159,7 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   if (misaligned(workspace, 256))
     return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, D, scale, causal, dtype,
-                (hipStream_t)stream, drop};
+                (hipStream_t)stream, drop, H_kv};
   return hip_status(fa::launch_backward(a, ws), who);
 }
 
@@ -251,8 +264,8 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
                      int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
                      void* stream) {
   g_last_error[0] = '\0';
-  return forward_impl(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, stream, fa::DropParams{},
-                      "fa_forward");
+  return forward_impl(q, k, v, o, lse, B, H, H, N, D, scale, causal, dtype, stream,
+                      fa::DropParams{}, "fa_forward");
 }
 
 fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -263,8 +276,22 @@ fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* 
   fa::DropParams dp;
   fa_status s = drop_params(dropout_p, seed, offset, dtype, "fa_forward_dropout", &dp);
   if (s != FA_OK) return s;
-  return forward_impl(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, stream, dp,
+  return forward_impl(q, k, v, o, lse, B, H, H, N, D, scale, causal, dtype, stream, dp,
                       "fa_forward_dropout");
+}
+
+fa_status fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, float scale,
+                         int causal, int dtype, float dropout_p, uint64_t seed, uint64_t offset,
+                         void* stream) {
+  g_last_error[0] = '\0';
+  const char* who = "fa_forward_gqa";
+  fa::DropParams dp{};
+  if (dropout_p != 0.f) {
+    fa_status s = drop_params(dropout_p, seed, offset, dtype, who, &dp);
+    if (s != FA_OK) return s;
+  }
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, N, D, scale, causal, dtype, stream, dp, who);
 }
 
 fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -299,8 +326,8 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
                       int64_t D, float scale, int causal, int dtype, void* stream) {
   g_last_error[0] = '\0';
-  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
-                       scale, causal, dtype, stream, fa::DropParams{}, "fa_backward");
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
+                       D, scale, causal, dtype, stream, fa::DropParams{}, "fa_backward");
 }
 
 fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
@@ -312,8 +339,24 @@ fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const
   fa::DropParams dp;
   fa_status s = drop_params(dropout_p, seed, offset, dtype, "fa_backward_dropout", &dp);
   if (s != FA_OK) return s;
-  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, D,
-                       scale, causal, dtype, stream, dp, "fa_backward_dropout");
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
+                       D, scale, causal, dtype, stream, dp, "fa_backward_dropout");
+}
+
+fa_status fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                          int64_t H_kv, int64_t N, int64_t D, float scale, int causal, int dtype,
+                          float dropout_p, uint64_t seed, uint64_t offset, void* stream) {
+  g_last_error[0] = '\0';
+  const char* who = "fa_backward_gqa";
+  fa::DropParams dp{};
+  if (dropout_p != 0.f) {
+    fa_status s = drop_params(dropout_p, seed, offset, dtype, who, &dp);
+    if (s != FA_OK) return s;
+  }
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv,
+                       N, D, scale, causal, dtype, stream, dp, who);
 }
 
 fa_status fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
@@ -360,7 +403,7 @@ fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const
   g_last_error[0] = '\0';
   const char* who = "fa_backward_noalloc";
   fa::BwdWorkspace ws;
-  fa_status s = check_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, dtype, who,
+  fa_status s = check_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, D, scale, dtype, who,
                                &ws);
   if (s != FA_OK) return s;
   if (ws.total > kScratchBytes)
@@ -372,7 +415,7 @@ fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const
   s = scratch_address(stream, &ptr, who);
   if (s != FA_OK) return s;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ptr, B, H, N, D, scale, causal, dtype,
-                (hipStream_t)stream, fa::DropParams{}};
+                (hipStream_t)stream, fa::DropParams{}, H};
   return hip_status(fa::launch_backward(a, ws), who);
 }
 

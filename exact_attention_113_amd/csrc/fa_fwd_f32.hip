@@ -27,7 +27,8 @@ constexpr float kTau = 8.0f;
 template <int D, bool CAUSAL, int KS>
 __global__ __launch_bounds__(64 * f32_row_groups(KS) * KS, 1) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, float c, float qsgn) {
+    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, float c, float qsgn,
+    int heads, int group) {
   constexpr int NRG = f32_row_groups(KS);  // row groups
   constexpr int kThreads = 64 * NRG * KS;
   constexpr int BM = 32 * NRG;              // query rows per workgroup
@@ -53,10 +54,13 @@ __global__ __launch_bounds__(64 * f32_row_groups(KS) * KS, 1) void fwd_f32_kerne
   int qt, bh;
   f32_tile_of(blockIdx.x, gridDim.x, n_qtiles, qt, bh);
   const int q0 = qt * BM;
+  // (batch, query head) pair bh; query head h reads K/V head h / group.
   const size_t head = (size_t)bh * (size_t)N * D;
+  const int b = bh / heads, h = bh - b * heads;
+  const size_t kv_head = ((size_t)b * (heads / group) + h / group) * (size_t)N * D;
   const float* Qh = Q + head;
-  const float* Kh = K + head;
-  const float* Vh = V + head;
+  const float* Kh = K + kv_head;
+  const float* Vh = V + kv_head;
 
   const int qw0 = q0 + 32 * rg;
   const int qi = qw0 + lq;
@@ -235,7 +239,7 @@ hipError_t launch_f32(const FwdArgs& a, const F32Shape& sh) {
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, KS>), dim3((unsigned)sh.grid),
                      dim3(64 * f32_row_groups(KS) * KS), 0, a.stream, (const float*)a.q,
                      (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.N,
-                     sh.n_qtiles, c, qsgn);
+                     sh.n_qtiles, c, qsgn, (int)a.H, (int)(a.H / (a.H_kv > 0 ? a.H_kv : a.H)));
   return hipGetLastError();
 }
 

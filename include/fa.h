@@ -130,6 +130,31 @@ fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* 
                              void* stream);
 
 /*
+ * fa_forward_gqa - fa_forward (and fa_forward_dropout) with grouped K/V
+ * heads in the dense layout: H query heads share H_kv K/V heads, query head
+ * h reading K/V head h / (H / H_kv) (MQA: H_kv = 1). Shared K/V heads are one
+ * of the factors the decode and prefill gains depend on ("Flash Attention
+ * algorithm design and I/O optimisation", "Training and inference value");
+ * each query head is still exact attention against its K/V head.
+ *
+ *   q         in   [B, H, N, D] of `dtype`
+ *   k, v      in   [B, H_kv, N, D] of `dtype`
+ *   o, lse    out  as for fa_forward
+ *   H_kv      divides H (H_kv = H is exactly fa_forward)
+ *   dropout_p 0 = no dropout (any dtype); otherwise as for
+ *             fa_forward_dropout (FA_FP16 or FA_BF16; the bits of query
+ *             head h of batch b are those of head b * H + h)
+ *   seed, offset  as for fa_forward_dropout (ignored when dropout_p = 0)
+ *   other arguments as for fa_forward
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, float scale,
+                         int causal, int dtype, float dropout_p, uint64_t seed, uint64_t offset,
+                         void* stream);
+
+/*
  * fa_forward_varlen - fused attention forward over a packed batch of
  * variable-length sequences, with grouped K/V heads (GQA/MQA).
  *
@@ -224,6 +249,30 @@ fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const
                               void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
                               int64_t N, int64_t D, float scale, int causal, int dtype,
                               float dropout_p, uint64_t seed, uint64_t offset, void* stream);
+
+/*
+ * fa_backward_gqa - backward of fa_forward_gqa (with or without dropout).
+ * Per query head the formulas of fa_backward (fa_backward_dropout when
+ * dropout_p != 0) hold; a K/V head serves H / H_kv query heads, so its dK
+ * and dV are the sums of their contributions (the chain rule through the
+ * shared operand), accumulated in fp32 in a fixed order (deterministic).
+ *
+ *   q, o, dout, dq   [B, H, N, D] of `dtype`
+ *   k, v, dk, dv     [B, H_kv, N, D] of `dtype`
+ *   lse              [B, H, N] fp32 from fa_forward_gqa
+ *   workspace        fa_backward_workspace_bytes(B, H, N, D) bytes
+ *   dropout_p, seed, offset  the values given to fa_forward_gqa
+ *   dtype            FA_FP16 or FA_BF16 (FA_FP32 returns FA_ERR_UNSUPPORTED)
+ *   other arguments as for fa_backward
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED,
+ * FA_ERR_WORKSPACE or FA_ERR_HIP.
+ */
+fa_status fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                          int64_t H_kv, int64_t N, int64_t D, float scale, int causal, int dtype,
+                          float dropout_p, uint64_t seed, uint64_t offset, void* stream);
 
 /*
  * fa_backward_varlen - backward of fa_forward_varlen: the gradients of a

@@ -281,3 +281,39 @@ def test_backward_noalloc_rejects_before_any_device_work():
     assert call(B=1, H=256, N=8192 + 1) == _lib.FA_ERR_UNSUPPORTED
     assert "scratch" in _lib.last_error()
     assert call(B=3, H=1 << 20, N=1) == _lib.FA_ERR_UNSUPPORTED
+
+
+def fwd_gqa(H=8, H_kv=2, p=0.0, dtype=2, D=64, q=A):
+    return _lib.load().fa_forward_gqa(q, A, A, A, A, 1, H, H_kv, 64, D, 0.125, 1, dtype, p, 1, 0,
+                                      None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H_kv=3), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H_kv=16), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(H_kv=-2), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(p=1.0), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(p=float("nan")), _lib.FA_ERR_INVALID_ARGUMENT),
+    (dict(p=0.1, dtype=0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_forward_gqa_validation(kw, status):
+    """Grouped K/V heads: H_kv must divide H; dropout as in fa_forward_dropout
+    (fp32 only without it). All rejected before any device work."""
+    assert fwd_gqa(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_backward_gqa_validation():
+    lib = _lib.load()
+
+    def call(H=8, H_kv=2, p=0.0, ws=A, dtype=2):
+        return lib.fa_backward_gqa(A, A, A, A, A, A, A, A, A, ws, 1 << 30, 1, H, H_kv, 64, 64,
+                                   0.125, 1, dtype, p, 0, 0, None)
+    assert call(H_kv=3) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert call(H_kv=0) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert call(p=1.5) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert call(dtype=0) == _lib.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.FA_ERR_WORKSPACE

@@ -45,3 +45,23 @@ def test_workspace_checks():
         fa._check_workspace("ws", torch.empty(100, dtype=torch.float32), 100, CPU)
     with pytest.raises(ValueError, match="uint8"):
         fa._check_workspace("ws", torch.empty(10, 10, dtype=torch.uint8), 100, CPU)
+
+
+@pytest.mark.parametrize("k_heads", [0, 3, 16])
+def test_grouped_heads_must_divide(k_heads):
+    """k and v may have H_kv heads only when H_kv divides H (checked before
+    any device or library call)."""
+    q = torch.zeros((1, 8, 16, 64))
+    k = torch.zeros((1, k_heads, 16, 64))
+    with pytest.raises(ValueError, match="H_kv"):
+        fa.forward(q, k, k.clone())
+    with pytest.raises(ValueError, match="H_kv"):
+        fa.backward(q, k, k.clone(), q, torch.zeros((1, 8, 16)), q)
+
+
+def test_grouped_heads_need_equal_k_and_v():
+    q = torch.zeros((1, 8, 16, 64))
+    with pytest.raises(ValueError):
+        fa.forward(q, torch.zeros((1, 2, 16, 64)), torch.zeros((1, 4, 16, 64)))
+    with pytest.raises(ValueError):
+        fa.forward(q, torch.zeros((1, 2, 8, 64)), torch.zeros((1, 2, 8, 64)))
