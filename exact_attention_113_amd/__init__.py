@@ -123,7 +123,7 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, dropout_p=0.0
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out=None,
-                   lse=None):
+                   lse=None, dropout_p=0.0, seed=0, offset=0):
     """Forward over a packed batch of variable-length sequences with grouped K/V heads.
 
     q: [total, H, D]; k, v: [total, H_kv, D] (H_kv divides H); cu_seqlens: int32
@@ -132,6 +132,8 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, ou
     offsets stay on the device (no synchronisation), so a longer sequence is
     not detected; it is cut to its first max_seqlen tokens and its later rows
     are not written.
+    dropout_p > 0 drops probabilities as `forward` does, with the bits of a
+    dense batch of the same sequences.
     Returns (o [total, H, D], lse fp32 [H, total]).
     """
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[0] != k.shape[0] \
@@ -158,12 +160,17 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, ou
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
     _check_buffer("lse", lse, (H, total), torch.float32, q.device)
     lib = _lib.load()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), total, H, k.shape[1],
+            D, float(scale), int(bool(causal)), _DTYPES[q.dtype])
     with torch.cuda.device(q.device):
-        st = lib.fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
-                                   int(max_seqlen), total, H, k.shape[1], D, float(scale),
-                                   int(bool(causal)), _DTYPES[q.dtype], _stream_handle(q))
-    _lib.check("fa_forward_varlen", st)
+        if dropout_p:
+            st = lib.fa_forward_varlen_dropout(*args, float(dropout_p), int(seed), int(offset),
+                                               _stream_handle(q))
+            _lib.check("fa_forward_varlen_dropout", st)
+        else:
+            st = lib.fa_forward_varlen(*args, _stream_handle(q))
+            _lib.check("fa_forward_varlen", st)
     return out, lse
 
 
@@ -276,8 +283,9 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, drop
 
 
 def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=None,
-                    workspace=None, out=None):
-    """Backward of forward_varlen from its o and lse [H, total]. Returns
+                    workspace=None, out=None, dropout_p=0.0, seed=0, offset=0):
+    """Backward of forward_varlen from its o and lse [H, total] (and its
+    dropout arguments). Returns
     (dq [total, H, D], dk, dv [total, H_kv, D]); dk and dv sum over the query
     heads that share each K/V head. `out` may give the three output tensors
     (rows of tokens outside every sequence are left as they are)."""
@@ -315,14 +323,18 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, s
         for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
             _check_buffer(name, t, ref.shape, ref.dtype, q.device)
     lib = _lib.load()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), cu_seqlens.numel() - 1, int(max_seqlen),
+            total, H, k.shape[1], D, float(scale), int(bool(causal)), _DTYPES[q.dtype])
     with torch.cuda.device(q.device):
-        st = lib.fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                    dv.data_ptr(), cu_seqlens.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel(), cu_seqlens.numel() - 1, int(max_seqlen),
-                                    total, H, k.shape[1], D, float(scale), int(bool(causal)),
-                                    _DTYPES[q.dtype], _stream_handle(q))
-    _lib.check("fa_backward_varlen", st)
+        if dropout_p:
+            st = lib.fa_backward_varlen_dropout(*args, float(dropout_p), int(seed), int(offset),
+                                                _stream_handle(q))
+            _lib.check("fa_backward_varlen_dropout", st)
+        else:
+            st = lib.fa_backward_varlen(*args, _stream_handle(q))
+            _lib.check("fa_backward_varlen", st)
     return dq, dk, dv
 
 
@@ -353,23 +365,29 @@ def attention(q, k, v, causal=False, scale=None, dropout_p=0.0, seed=0, offset=0
 
 class _FlashAttentionVarlen(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, scale):
-        o, lse = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale)
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, scale, dropout_p, seed, offset):
+        o, lse = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale,
+                                dropout_p=dropout_p, seed=seed, offset=offset)
         ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
         ctx.max_seqlen, ctx.causal, ctx.scale = max_seqlen, causal, scale
+        ctx.dropout = (dropout_p, seed, offset)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, cu = ctx.saved_tensors
+        p, seed, offset = ctx.dropout
         dq, dk, dv = backward_varlen(q, k, v, o, lse, do.contiguous(), cu, ctx.max_seqlen,
-                                     ctx.causal, ctx.scale)
-        return dq, dk, dv, None, None, None, None
+                                     ctx.causal, ctx.scale, dropout_p=p, seed=seed,
+                                     offset=offset)
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
-def attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None):
+def attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, dropout_p=0.0,
+                     seed=0, offset=0):
     """Autograd-aware fused attention over a packed variable-length batch with
-    grouped K/V heads (O only)."""
+    grouped K/V heads (O only), with optional dropout."""
     if scale is None:
         scale = default_scale(q.shape[-1])
-    return _FlashAttentionVarlen.apply(q, k, v, cu_seqlens, max_seqlen, causal, scale)
+    return _FlashAttentionVarlen.apply(q, k, v, cu_seqlens, max_seqlen, causal, scale, dropout_p,
+                                       seed, offset)

@@ -34,6 +34,11 @@ PROTOTYPES = {
                                       _I, _F, _U64, _U64, _P]),
     "fa_backward_gqa": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64,
                                        _I64, _I64, _I64, _F, _I, _I, _F, _U64, _U64, _P]),
+    "fa_forward_varlen_dropout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                                 _I64, _I64, _F, _I, _I, _F, _U64, _U64, _P]),
+    "fa_backward_varlen_dropout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                                  _I64, _I64, _I64, _I64, _I64, _I64, _F, _I, _I,
+                                                  _F, _U64, _U64, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
 }

@@ -257,6 +257,62 @@ fa_status scratch_address(void* stream, void** out, const char* who) {
 
 }  // namespace
 
+// The packed-batch forward and backward (with dropout when drop.thr != 0).
+fa_status forward_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* cu_seqlens, int64_t batch, int64_t max_seqlen,
+                              int64_t total, int64_t H, int64_t H_kv, int64_t D, float scale,
+                              int causal, int dtype, void* stream, const fa::DropParams& drop,
+                              const char* who) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o, lse and cu_seqlens must be non-NULL",
+                who);
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o must be 16-byte aligned", who);
+  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse and cu_seqlens must be 4-byte aligned", who);
+  fa_status s = check_varlen(batch, max_seqlen, total, H, H_kv, D, scale, dtype, who);
+  if (s != FA_OK) return s;
+  fa::FwdArgs a{q,     k,      v,     o,      lse,        batch, H,     max_seqlen, D,
+                scale, causal, dtype, (hipStream_t)stream, H_kv, cu_seqlens, total, drop};
+  return hip_status(fa::launch_forward(a), who);
+}
+
+fa_status backward_varlen_impl(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               const int32_t* cu_seqlens, void* workspace,
+                               size_t workspace_bytes, int64_t batch, int64_t max_seqlen,
+                               int64_t total, int64_t H, int64_t H_kv, int64_t D, float scale,
+                               int causal, int dtype, void* stream, const fa::DropParams& drop,
+                               const char* who) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "%s: q, k, v, o, dout, lse, dq, dk, dv and cu_seqlens must be non-NULL", who);
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: tensors must be 16-byte aligned", who);
+  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse and cu_seqlens must be 4-byte aligned", who);
+  fa_status s = check_varlen(batch, max_seqlen, total, H, H_kv, D, scale, dtype, who);
+  if (s != FA_OK) return s;
+  if (total > (int64_t)0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "%s: total (%lld) above 2^31 - 1", who, (long long)total);
+  fa::BwdWorkspace ws;
+  if (!fa::backward_workspace_layout(1, H, total, D, &ws))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace size overflows", who);
+  if (!workspace)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace is NULL (needs %lld bytes)", who,
+                (long long)ws.total);
+  if (workspace_bytes < ws.total)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace too small (needs %lld bytes)", who,
+                (long long)ws.total);
+  if (misaligned(workspace, 256))
+    return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+  fa::BwdArgs a{q,     k,      v,     o,      dout,  lse,       dq,        dk,
+                dv,    workspace, batch, H,     max_seqlen, D,  scale,     causal,
+                dtype, (hipStream_t)stream, drop, H_kv, cu_seqlens, total};
+  return hip_status(fa::launch_backward(a, ws), who);
+}
+
 extern "C" {
 
 
@@ -299,20 +355,23 @@ fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o
                             int64_t total, int64_t H, int64_t H_kv, int64_t D, float scale,
                             int causal, int dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (!q || !k || !v || !o || !lse || !cu_seqlens)
-    return fail(FA_ERR_INVALID_ARGUMENT,
-                "fa_forward_varlen: q, k, v, o, lse and cu_seqlens must be non-NULL");
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_forward_varlen: q, k, v, o must be 16-byte aligned");
-  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
-    return fail(FA_ERR_INVALID_ARGUMENT,
-                "fa_forward_varlen: lse and cu_seqlens must be 4-byte aligned");
-  fa_status s = check_varlen(batch, max_seqlen, total, H, H_kv, D, scale, dtype,
-                             "fa_forward_varlen");
+  return forward_varlen_impl(q, k, v, o, lse, cu_seqlens, batch, max_seqlen, total, H, H_kv, D,
+                             scale, causal, dtype, stream, fa::DropParams{}, "fa_forward_varlen");
+}
+
+fa_status fa_forward_varlen_dropout(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int32_t* cu_seqlens, int64_t batch,
+                                    int64_t max_seqlen, int64_t total, int64_t H, int64_t H_kv,
+                                    int64_t D, float scale, int causal, int dtype,
+                                    float dropout_p, uint64_t seed, uint64_t offset,
+                                    void* stream) {
+  g_last_error[0] = '\0';
+  const char* who = "fa_forward_varlen_dropout";
+  fa::DropParams dp;
+  fa_status s = drop_params(dropout_p, seed, offset, dtype, who, &dp);
   if (s != FA_OK) return s;
-  fa::FwdArgs a{q,     k,      v,     o,      lse,        batch, H,     max_seqlen, D,
-                scale, causal, dtype, (hipStream_t)stream, H_kv, cu_seqlens, total};
-  return hip_status(fa::launch_forward(a), "fa_forward_varlen");
+  return forward_varlen_impl(q, k, v, o, lse, cu_seqlens, batch, max_seqlen, total, H, H_kv, D,
+                             scale, causal, dtype, stream, dp, who);
 }
 
 size_t fa_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
@@ -366,34 +425,26 @@ fa_status fa_backward_varlen(const void* q, const void* k, const void* v, const 
                              int64_t H_kv, int64_t D, float scale, int causal, int dtype,
                              void* stream) {
   g_last_error[0] = '\0';
-  const char* who = "fa_backward_varlen";
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
-    return fail(FA_ERR_INVALID_ARGUMENT,
-                "%s: q, k, v, o, dout, lse, dq, dk, dv and cu_seqlens must be non-NULL", who);
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
-      misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
-    return fail(FA_ERR_INVALID_ARGUMENT, "%s: tensors must be 16-byte aligned", who);
-  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4))
-    return fail(FA_ERR_INVALID_ARGUMENT, "%s: lse and cu_seqlens must be 4-byte aligned", who);
-  fa_status s = check_varlen(batch, max_seqlen, total, H, H_kv, D, scale, dtype, who);
+  return backward_varlen_impl(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace,
+                              workspace_bytes, batch, max_seqlen, total, H, H_kv, D, scale,
+                              causal, dtype, stream, fa::DropParams{}, "fa_backward_varlen");
+}
+
+fa_status fa_backward_varlen_dropout(const void* q, const void* k, const void* v, const void* o,
+                                     const void* dout, const float* lse, void* dq, void* dk,
+                                     void* dv, const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, int64_t batch, int64_t max_seqlen,
+                                     int64_t total, int64_t H, int64_t H_kv, int64_t D,
+                                     float scale, int causal, int dtype, float dropout_p,
+                                     uint64_t seed, uint64_t offset, void* stream) {
+  g_last_error[0] = '\0';
+  const char* who = "fa_backward_varlen_dropout";
+  fa::DropParams dp;
+  fa_status s = drop_params(dropout_p, seed, offset, dtype, who, &dp);
   if (s != FA_OK) return s;
-  if (total > (int64_t)0x7fffffff)
-    return fail(FA_ERR_UNSUPPORTED, "%s: total (%lld) above 2^31 - 1", who, (long long)total);
-  fa::BwdWorkspace ws;
-  if (!fa::backward_workspace_layout(1, H, total, D, &ws))
-    return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace size overflows", who);
-  if (!workspace)
-    return fail(FA_ERR_WORKSPACE, "%s: workspace is NULL (needs %lld bytes)", who,
-                (long long)ws.total);
-  if (workspace_bytes < ws.total)
-    return fail(FA_ERR_WORKSPACE, "%s: workspace too small (needs %lld bytes)", who,
-                (long long)ws.total);
-  if (misaligned(workspace, 256))
-    return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
-  fa::BwdArgs a{q,     k,      v,     o,      dout,  lse,       dq,        dk,
-                dv,    workspace, batch, H,     max_seqlen, D,  scale,     causal,
-                dtype, (hipStream_t)stream, fa::DropParams{}, H_kv, cu_seqlens, total};
-  return hip_status(fa::launch_backward(a, ws), who);
+  return backward_varlen_impl(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace,
+                              workspace_bytes, batch, max_seqlen, total, H, H_kv, D, scale,
+                              causal, dtype, stream, dp, who);
 }
 
 fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,

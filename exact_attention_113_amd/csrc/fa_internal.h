@@ -36,7 +36,7 @@ struct FwdArgs {
   int64_t H_kv;
   const int32_t* cu_seqlens;
   int64_t total;
-  DropParams drop;   // thr = 0: none (dense batches only)
+  DropParams drop;   // thr = 0: none
 };
 
 struct BwdArgs {

@@ -190,6 +190,25 @@ fa_status fa_forward_varlen(const void* q, const void* k, const void* v, void* o
                             int causal, int dtype, void* stream);
 
 /*
+ * fa_forward_varlen_dropout - fa_forward_varlen with dropout on the
+ * attention probabilities, as fa_forward_dropout defines it for each
+ * (sequence, query head): element (i, j) of query head h of sequence b, i
+ * and j counted from the sequence's first token, takes the bits of head
+ * b * H + h (exactly those of a dense batch of the same sequences).
+ *
+ *   dropout_p, seed, offset  as for fa_forward_dropout
+ *   other arguments as for fa_forward_varlen
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_forward_varlen_dropout(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int32_t* cu_seqlens, int64_t batch,
+                                    int64_t max_seqlen, int64_t total, int64_t H, int64_t H_kv,
+                                    int64_t D, float scale, int causal, int dtype,
+                                    float dropout_p, uint64_t seed, uint64_t offset,
+                                    void* stream);
+
+/*
  * fa_backward_workspace_bytes - device workspace fa_backward needs for
  * this shape: two fp32 row statistics [B, H, N] (delta = rowsum(dO * O) and
  * LSE * log2(e)), each padded to 256 bytes (the two-phase workspace query of
@@ -307,6 +326,21 @@ fa_status fa_backward_varlen(const void* q, const void* k, const void* v, const 
                              int64_t batch, int64_t max_seqlen, int64_t total, int64_t H,
                              int64_t H_kv, int64_t D, float scale, int causal, int dtype,
                              void* stream);
+
+/*
+ * fa_backward_varlen_dropout - backward of fa_forward_varlen_dropout: the
+ * formulas of fa_backward_dropout per (sequence, query head), dK and dV
+ * summed over each K/V head's query heads as in fa_backward_varlen. The
+ * dropout arguments must be those given to the forward. Workspace,
+ * arguments and statuses as for fa_backward_varlen.
+ */
+fa_status fa_backward_varlen_dropout(const void* q, const void* k, const void* v, const void* o,
+                                     const void* dout, const float* lse, void* dq, void* dk,
+                                     void* dv, const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, int64_t batch, int64_t max_seqlen,
+                                     int64_t total, int64_t H, int64_t H_kv, int64_t D,
+                                     float scale, int causal, int dtype, float dropout_p,
+                                     uint64_t seed, uint64_t offset, void* stream);
 
 /*
  * fa_decode_workspace_bytes - device workspace fa_decode needs for these

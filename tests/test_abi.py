@@ -317,3 +317,25 @@ def test_backward_gqa_validation():
     assert call(p=1.5) == _lib.FA_ERR_INVALID_ARGUMENT
     assert call(dtype=0) == _lib.FA_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.FA_ERR_WORKSPACE
+
+
+def test_varlen_dropout_validation():
+    """The packed dropout entry points validate the dropout arguments as the
+    dense ones do, and the packed arguments as fa_forward_varlen does, before
+    any device work."""
+    lib = _lib.load()
+
+    def fwd(p=0.1, H_kv=2, dtype=2, offset=0):
+        return lib.fa_forward_varlen_dropout(A, A, A, A, A, A, 2, 64, 128, 4, H_kv, 64, 0.125, 1,
+                                             dtype, p, 1, offset, None)
+
+    def bwd(p=0.1, ws=A):
+        return lib.fa_backward_varlen_dropout(A, A, A, A, A, A, A, A, A, A, ws, 1 << 30, 2, 64,
+                                              128, 4, 2, 64, 0.125, 1, 2, p, 1, 0, None)
+    assert fwd(p=1.0) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert fwd(p=float("nan")) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert fwd(offset=1 << 32) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert fwd(H_kv=3) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert fwd(dtype=0) == _lib.FA_ERR_UNSUPPORTED
+    assert bwd(p=-0.5) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert bwd(ws=None) == _lib.FA_ERR_WORKSPACE
