@@ -99,6 +99,7 @@ struct FwdParams {
   int group;          // query heads per K/V head
   int n_qtiles;
   int bh_count;
+  int pair_order;     // pairwise XCD order of the tiles (fwd_tile_of)
   float c;
   uint32_t qsign;
   DropParams drop;    // dense batches only
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   const float c = prm.c;
   const uint32_t qsign = prm.qsign;
   int qt, p;
-  fwd_tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, qt, p);
+  fwd_tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, prm.pair_order != 0, qt, p);
   // This (sequence, head): its length N, the element offsets of its first
   // Q/O and K/V rows and of its LSE entries, and the row strides.
   const int batch = prm.bh_count / prm.heads;
@@ -687,6 +688,7 @@ hipError_t launch_half(const FwdArgs& a) {
   p.diag = a.causal ? 0 : (int)a.N;
   const FwdShape sh = fwd_shape(p.bh_count, a.N, a.causal != 0, D);
   p.n_qtiles = sh.n_qtiles;
+  p.pair_order = sh.pairs && a.cu_seqlens == nullptr;
   auto go = [&](auto ks) {
     constexpr int KS = decltype(ks)::value;
     const dim3 grid((unsigned)sh.grid);

@@ -110,7 +110,7 @@ void check_forward_d(const std::string& name, const Batch& x, int H, int Hkv, bo
   const int64_t n_stat = rows_of(x, H);
   for (int lin = 0; lin < (int)sh.grid; ++lin) {
     int qt, p;
-    fa::fwd_tile_of(lin, sh.n_qtiles, bh_count, qt, p);
+    fa::fwd_tile_of(lin, sh.n_qtiles, bh_count, sh.pairs && !x.packed, qt, p);
     CHECK(p >= 0 && p < bh_count && qt >= 0 && qt < sh.n_qtiles, "lin %d -> qt %d p %d", lin, qt,
           p);
     const int h = p / batch, b = p - h * batch, hk = h / group;
@@ -137,8 +137,8 @@ void check_forward_d(const std::string& name, const Batch& x, int H, int Hkv, bo
   }
   std::string why;
   CHECK(exactly_once(x, H, cover, why), "%s", why.c_str());
-  std::printf("ok %s D%d: %lld workgroups, key split %d\n", name.c_str(), d, (long long)sh.grid,
-              sh.ks);
+  std::printf("ok %s D%d: %lld workgroups, key split %d%s\n", name.c_str(), d,
+              (long long)sh.grid, sh.ks, sh.pairs && !x.packed ? ", pairwise order" : "");
 }
 
 // Both head dims: their grid rules differ for the shortest grids.
@@ -157,7 +157,7 @@ void check_malformed(const std::string& name, const std::vector<int32_t>& cu, in
   const fa::FwdShape sh = fa::fwd_shape(batch * H, x.seqlen, causal, d);
   for (int lin = 0; lin < (int)sh.grid; ++lin) {
     int qt, p;
-    fa::fwd_tile_of(lin, sh.n_qtiles, batch * H, qt, p);
+    fa::fwd_tile_of(lin, sh.n_qtiles, batch * H, false, qt, p);
     const int h = p / batch, b = p - h * batch;
     int s0, n;
     span(x, b, s0, n);
@@ -337,6 +337,7 @@ int main() {
     check_forward("fwd B8 H16 N1000" + c, dense(8, 1000), 16, 16, causal);
     check_forward("fwd B4096 H32 N128" + c, dense(4096, 128), 32, 32, causal);
     check_forward("fwd B1 H2 N131072" + c, dense(1, 131072), 2, 2, causal);
+    check_forward("fwd B2 H32 N4000" + c, dense(2, 4000), 32, 32, causal);  // pairwise, ragged
   }
   // Packed batches: empty, one-token and ragged sequences, grouped heads,
   // tokens after the last sequence, the packed prefill workload's lengths.

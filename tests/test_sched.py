@@ -42,6 +42,8 @@ MUTANTS = {
     "xcd_slot_halved": ("return (lin & 7) * (total >> 3) + (lin >> 3);",
                         "return (lin & 7) * (total >> 3) + (lin >> 4);"),
     "fwd_pair_off": ("p = xcd * hpx + slot % hpx;", "p = xcd * hpx + slot / hpx;"),
+    "fwd_pairwise_head": ("p = xcd * hpx + 2 * j + (within & 1);", "p = xcd * hpx + j + (within & 1);"),
+    "fwd_pairwise_tile": ("qt = n_qtiles - 1 - within / 2;", "qt = n_qtiles - 1 - within / 4;"),
     "packed_tile_off_by_one": ("return packed ? qt - (n_qtiles - (n + bm - 1) / bm) : qt;",
                                "return packed ? qt - (n_qtiles - n / bm) : qt;"),
     "dq_tile_bound": ("return (qt < 0 || qt * bm >= n) ? -1 : qt;",
