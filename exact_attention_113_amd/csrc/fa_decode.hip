@@ -133,6 +133,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecParams 
   const int L = min(max(prm.seqlens[b], 0), prm.max_len);
   const int k_lo = split * prm.chunk;
   const int k_hi = min(L, k_lo + prm.chunk);
+  // Chunks past the cached keys write nothing: the merge weighs only the
+  // first ones.
+  if (split >= decode_active_chunks(L, prm.chunk, prm.n_splits)) return;
   const int nblk = k_hi > k_lo ? (k_hi - k_lo + kDKB - 1) / kDKB : 0;
   const int rows = prm.group * prm.s_q;
 
@@ -421,6 +424,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode16_kernel(const DecParam
   const int L = min(max(prm.seqlens[b], 0), prm.max_len);
   const int k_lo = split * prm.chunk;
   const int k_hi = min(L, k_lo + prm.chunk);
+  // Chunks past the cached keys write nothing: the merge weighs only the
+  // first ones.
+  if (split >= decode_active_chunks(L, prm.chunk, prm.n_splits)) return;
   const int nblk = k_hi > k_lo ? (k_hi - k_lo + kDKB - 1) / kDKB : 0;
   const int rows = prm.group * prm.s_q;
 
@@ -667,40 +673,54 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Combine the chunks of one output row (b, h, t), one wave per row:
-// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s; chunks with
-// LSE_s = -inf carry no weight, and a row with none left is O = 0,
-// LSE = -inf. Lane s holds chunk s's LSE and weight (at most 64 chunks);
-// the partial outputs are loaded 32 chunks at a time before any is
-// used, so the loads overlap.
+// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s over the chunks
+// that hold keys (the others wrote nothing); chunks with LSE_s = -inf carry
+// no weight, and a row with none left is O = 0, LSE = -inf. Lane s holds
+// chunk s's LSE and weight (at most 64 chunks). Once the sequence length
+// gives the number of active chunks, their LSEs and the partial outputs of
+// the first 32 of them are loaded together, before any is used (slots past
+// the active chunks re-read the last one and get weight 0), so the partial
+// results cost one memory round trip.
 template <typename TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
+                                                           const int32_t* __restrict__ seqlens,
                                                            uint16_t* __restrict__ o,
                                                            float* __restrict__ lse, int n_rows,
-                                                           int n_splits, int heads, int s_q) {
+                                                           int n_splits, int chunk, int max_len,
+                                                           int heads, int s_q) {
   constexpr int PER = D / 64;
   constexpr int U = 32;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;
-  const float ls = lane < n_splits ? part_lse[(size_t)row * n_splits + lane] : -INFINITY;
+  const int t = row % s_q, bh = row / s_q;
+  const int b = bh / heads, h = bh - b * heads;
+  const int na = decode_active_chunks(min(max(seqlens[b], 0), max_len), chunk, n_splits);
+  const float ls = lane < na ? part_lse[(size_t)row * n_splits + lane] : -INFINITY;
+  const float* src = part_o + (size_t)row * n_splits * D + lane * PER;
+  float val[U][PER];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) val[u][e] = src[(size_t)min(u, na - 1) * D + e];
   const float m = wave_max(ls);
   const float wt = (ls == -INFINITY) ? 0.f : __expf(ls - m);
   const float wsum = wave_sum(wt);
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  const float* src = part_o + (size_t)row * n_splits * D + lane * PER;
-  for (int s0 = 0; s0 < n_splits; s0 += U) {
-    float val[U][PER];
+  for (int s0 = 0; s0 < na; s0 += U) {
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int e = 0; e < PER; ++e)
-        val[u][e] = s0 + u < n_splits ? src[(size_t)(s0 + u) * D + e] : 0.f;
+        for (int e = 0; e < PER; ++e)
+          val[u][e] = src[(size_t)min(s0 + u, na - 1) * D + e];
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float ws = s0 + u < n_splits
+      const float ws = s0 + u < na
                            ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                            __builtin_bit_cast(int, wt), s0 + u))
                            : 0.f;
@@ -709,8 +729,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int t = row % s_q, bh = row / s_q;
-  const int b = bh / heads, h = bh - b * heads;
   uint16_t* dst = o + ((size_t)(b * s_q + t) * heads + h) * D + lane * PER;
   if constexpr (PER == 2) {
     *(uint32_t*)dst = TT::pack2(acc[0] * inv, acc[1] * inv);
@@ -751,8 +769,8 @@ hipError_t launch_typed(const DecodeArgs& a, const DecodePlan& plan) {
   if (plan.n_splits > 1) {
     const int n_rows = (int)(a.B * a.H * a.s_q);
     hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((unsigned)((n_rows + 3) / 4)), dim3(256),
-                       0, a.stream, p.part_o, p.part_lse, p.o, p.lse, n_rows, plan.n_splits,
-                       p.heads, p.s_q);
+                       0, a.stream, p.part_o, p.part_lse, p.seqlens, p.o, p.lse, n_rows,
+                       plan.n_splits, p.chunk, p.max_len, p.heads, p.s_q);
   }
   return hipGetLastError();
 }

@@ -222,6 +222,16 @@ __host__ __device__ inline void decode_unit(int blk, int n_splits, int hkv, int&
   b = rest / n_splits;
 }
 
+// Chunks of a sequence with L visible cache keys (L already clamped to
+// [0, max_len]) that hold keys: chunks 0 .. result - 1 write a partial
+// result; the rest do nothing, and the merge weighs only the first ones. A
+// sequence with no key still has chunk 0 (it writes O = 0, LSE = -inf).
+__host__ __device__ inline int decode_active_chunks(int L, int chunk, int n_splits) {
+  if (L <= 0) return 1;
+  const int n = (L + chunk - 1) / chunk;
+  return n < n_splits ? n : n_splits;
+}
+
 // Workgroups the chunk plan aims for, and the most chunks per row (one
 // lane of the merge kernel's wave each).
 #ifndef FA_DECODE_TARGET_WGS

@@ -285,6 +285,7 @@ void check_decode(const std::string& name, int s_q, int H, int Hkv, int cap, int
   const int grid = B * Hkv * plan.n_splits;
   const int group = H / Hkv;
   std::vector<int> cover((size_t)B * Hkv * cap, 0);
+  std::vector<int> written((size_t)B * Hkv * plan.n_splits, 0);
   for (int blk = 0; blk < grid; ++blk) {
     int b, hk, split;
     fa::decode_unit(blk, plan.n_splits, Hkv, b, hk, split);
@@ -292,6 +293,14 @@ void check_decode(const std::string& name, int s_q, int H, int Hkv, int cap, int
           "blk %d", blk);
     const int L = std::min(std::max(lens[b], 0), max_len);
     const int k_lo = split * plan.chunk, k_hi = std::min(L, k_lo + plan.chunk);
+    // Chunks past the active ones return at once; they must hold no key.
+    const int na = fa::decode_active_chunks(L, plan.chunk, plan.n_splits);
+    CHECK(na >= 1 && na <= plan.n_splits, "%d active chunks", na);
+    if (split >= na) {
+      CHECK(k_hi <= k_lo, "skipped chunk %d of sequence %d holds keys", split, b);
+      continue;
+    }
+    if (plan.n_splits > 1) ++written[((size_t)b * Hkv + hk) * plan.n_splits + split];
     for (int k = k_lo; k < k_hi; ++k) {
       CHECK(k < cap, "key %d past the capacity %d", k, cap);
       ++cover[((size_t)b * Hkv + hk) * cap + k];
@@ -306,6 +315,15 @@ void check_decode(const std::string& name, int s_q, int H, int Hkv, int cap, int
   }
   for (int b = 0; b < B; ++b) {
     const int L = std::min(std::max(lens[b], 0), max_len);
+    // The merge weighs chunks [0, na) of each row: each is written once.
+    const int na = fa::decode_active_chunks(L, plan.chunk, plan.n_splits);
+    if (plan.n_splits > 1)
+      for (int hk = 0; hk < Hkv; ++hk)
+        for (int sp = 0; sp < plan.n_splits; ++sp) {
+          const int c = written[((size_t)b * Hkv + hk) * plan.n_splits + sp];
+          CHECK(c == (sp < na ? 1 : 0), "sequence %d head %d chunk %d written %d times", b, hk,
+                sp, c);
+        }
     for (int hk = 0; hk < Hkv; ++hk)
       for (int k = 0; k < cap; ++k) {
         const int c = cover[((size_t)b * Hkv + hk) * cap + k];

@@ -55,6 +55,7 @@ MUTANTS = {
     "decode_unit_swap": ("split = rest % n_splits;\n  b = rest / n_splits;",
                          "b = rest % n_splits;\n  split = rest / n_splits;"),
     "decode_chunk_round": ("chunk = (chunk + 127) / 128 * 128;", "chunk = chunk / 128 * 128;"),
+    "decode_active_floor": ("const int n = (L + chunk - 1) / chunk;", "const int n = L / chunk;"),
     "split_rows": ("s.bm = 256 / s.ks;", "s.bm = 128;"),
     "f32_split_rows": ("s.bm = 32 * f32_row_groups(s.ks);", "s.bm = 32 * f32_row_groups(1);"),
 }
