@@ -100,6 +100,7 @@ struct FwdParams {
   int n_qtiles;
   int bh_count;
   int pair_order;     // pairwise XCD order of the tiles (fwd_tile_of)
+  int lpt;            // packed: only real tiles, heaviest first (fwd_packed_lpt_wave)
   float c;
   uint32_t qsign;
   DropParams drop;    // dense batches only
@@ -157,12 +158,23 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
 
   const float c = prm.c;
   const uint32_t qsign = prm.qsign;
-  int qt, p;
-  fwd_tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, prm.pair_order != 0, qt, p);
+  // This workgroup's (sequence bidx, head h, query tile qt).
+  const int batch = prm.bh_count / prm.heads;
+  int qt, h, bidx;
+  if (prm.lpt) {
+    int hl;
+    if (!fwd_packed_lpt_wave(prm.cu, batch, prm.total, prm.seqlen, kBM, prm.n_qtiles,
+                             prm.heads >> 3, (int)(blockIdx.x >> 3), lane, bidx, hl, qt))
+      return;  // past the batch's last tile
+    h = (int)(blockIdx.x & 7) * (prm.heads >> 3) + hl;
+  } else {
+    int p;
+    fwd_tile_of(blockIdx.x, prm.n_qtiles, prm.bh_count, prm.pair_order != 0, qt, p);
+    h = p / batch;
+    bidx = p - h * batch;
+  }
   // This (sequence, head): its length N, the element offsets of its first
   // Q/O and K/V rows and of its LSE entries, and the row strides.
-  const int batch = prm.bh_count / prm.heads;
-  const int h = p / batch, bidx = p - h * batch;
   const int bh = bidx * prm.heads + h;
   const int hkv = prm.heads / prm.group, hk = h / prm.group;
   int N;
@@ -183,11 +195,13 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
     lbase = (size_t)bh * N;
     sq = skv = D;
   }
-  // Packed batches count a sequence's tiles back from its own last one, so
-  // that the slots past the end of shorter sequences (no work) come last in
-  // the dispatch order instead of first.
-  qt = fwd_seq_tile(qt, prm.n_qtiles, N, kBM, prm.cu != nullptr);
-  if (qt < 0) return;
+  // Without the whole-batch order, packed batches count a sequence's tiles
+  // back from its own last one, so that the slots past the end of shorter
+  // sequences (no work) come last in the dispatch order instead of first.
+  if (!prm.lpt) {
+    qt = fwd_seq_tile(qt, prm.n_qtiles, N, kBM, prm.cu != nullptr);
+    if (qt < 0) return;
+  }
   const int q0 = qt * kBM;
   const uint16_t* Qh = prm.q + qbase;
   const uint16_t* Kh = prm.k + kvbase;
@@ -689,9 +703,12 @@ hipError_t launch_half(const FwdArgs& a) {
   const FwdShape sh = fwd_shape(p.bh_count, a.N, a.causal != 0, D);
   p.n_qtiles = sh.n_qtiles;
   p.pair_order = sh.pairs && a.cu_seqlens == nullptr;
+  p.lpt = a.cu_seqlens != nullptr && fwd_packed_lpt_ok(a.B, a.H, sh.n_qtiles);
+  const int64_t grid_size =
+      p.lpt ? fwd_packed_lpt_grid(a.B, a.total, a.H, sh.bm, sh.n_qtiles) : sh.grid;
   auto go = [&](auto ks) {
     constexpr int KS = decltype(ks)::value;
-    const dim3 grid((unsigned)sh.grid);
+    const dim3 grid((unsigned)grid_size);
     if (a.drop.thr != 0)
       hipLaunchKernelGGL((fwd_kernel<TT, D, 8, true, KS>), grid, dim3(512), 0, a.stream, p);
     else

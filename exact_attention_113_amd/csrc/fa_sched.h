@@ -69,6 +69,94 @@ __host__ __device__ inline int fwd_seq_tile(int qt, int n_qtiles, int n, int bm,
   return packed ? qt - (n_qtiles - (n + bm - 1) / bm) : qt;
 }
 
+// Packed batches: a grid of only the batch's real tiles, heaviest first over
+// the whole batch. Tile t of a sequence (rows t * bm ..) orders it: under a
+// causal mask it sees t + 1 key tiles whatever its sequence, and with full
+// attention only sequences of more than t tiles have a tile t, so the high
+// indices belong to the longest sequences either way. Within one index the
+// heads vary fastest, then the sequences in order. Workgroup lin takes slot
+// s = lin >> 3 of XCD lin & 7, which owns heads (lin & 7) * H/8 .. + H/8 - 1
+// of every sequence as in the dense order (a K/V head's query heads share
+// its L2); slots past the batch's last tile exit at once. Measured on the
+// 16-sequence prefill batch (256..4096 tokens, H32/8, D128): 928-931 ->
+// 791-792 us causal and 1658-1663 -> 1414-1418 us with full attention
+// against the grid of (sequence, head) x the longest sequence's tiles, whose
+// empty workgroups each held a CU. The device form keeps one sequence's tile
+// count and one tile index per lane, hence the limits.
+constexpr int kLptMaxBatch = 64;
+constexpr int kLptMaxTiles = 64;
+inline bool fwd_packed_lpt_ok(int64_t batch, int64_t heads, int n_qtiles) {
+  return heads % 8 == 0 && batch <= kLptMaxBatch && n_qtiles <= kLptMaxTiles;
+}
+// Slots for every tile: the tiles number sum_b ceil(n_b / bm), at most
+// (total + batch (bm - 1)) / bm and batch * n_qtiles.
+inline int64_t fwd_packed_lpt_grid(int64_t batch, int64_t total, int64_t heads, int bm,
+                                   int n_qtiles) {
+  const int64_t bound = (total + batch * (bm - 1)) / bm;
+  const int64_t most = batch * (int64_t)n_qtiles;
+  return heads * (bound < most ? bound : most);
+}
+// Tiles of sequence b: ceil(n_b / bm) with n_b as the kernels see it.
+__host__ __device__ inline int packed_tiles(const int32_t* cu, int b, int total, int seqlen,
+                                            int bm) {
+  int s0, n;
+  seq_span(cu, b, total, seqlen, s0, n);
+  return (n + bm - 1) / bm;
+}
+// Slot s of an XCD with g8 heads: sequence b, head hl of the XCD's heads and
+// tile t; false past the last tile. This host form runs the device form's
+// steps over the 64 lanes one after another (lane j: sequence j's tile count,
+// and the count c[j] of the batch's tiles with index >= j).
+inline bool fwd_packed_lpt_host(const int32_t* cu, int batch, int total, int seqlen, int bm,
+                                int n_qtiles, int g8, int s, int& b, int& hl, int& t) {
+  int nt[64], c[64];
+  for (int l = 0; l < 64; ++l) nt[l] = l < batch ? packed_tiles(cu, l, total, seqlen, bm) : 0;
+  for (int l = 0; l < 64; ++l) {
+    c[l] = 0;
+    for (int j = 0; j < batch; ++j) c[l] += nt[j] - l > 0 ? nt[j] - l : 0;
+  }
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l) m |= (uint64_t)(l < n_qtiles && g8 * c[l] > s) << l;
+  if (m == 0) return false;
+  t = __builtin_popcountll(m) - 1;
+  const int i = s - g8 * (t + 1 < 64 ? c[t + 1] : 0);
+  hl = i % g8;
+  const int k = i / g8;
+  uint64_t m2 = 0;
+  for (int l = 0; l < 64; ++l) m2 |= (uint64_t)(l < batch && nt[l] > t) << l;
+  uint64_t m3 = 0;
+  for (int l = 0; l < 64; ++l) {
+    const int rank = __builtin_popcountll(m2 & ((1ull << l) - 1));
+    m3 |= (uint64_t)(((m2 >> l) & 1) && rank == k) << l;
+  }
+  b = m3 ? __builtin_ctzll(m3) : -1;
+  return b >= 0;
+}
+// The same on the device, lane l of the calling wave holding lane l's
+// values; every wave of a workgroup gets the same answer.
+__device__ inline bool fwd_packed_lpt_wave(const int32_t* cu, int batch, int total, int seqlen,
+                                           int bm, int n_qtiles, int g8, int s, int lane, int& b,
+                                           int& hl, int& t) {
+  const int nt = lane < batch ? packed_tiles(cu, lane, total, seqlen, bm) : 0;
+  int c = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int d = __builtin_amdgcn_readlane(nt, j) - lane;
+    c += d > 0 ? d : 0;
+  }
+  const uint64_t m = __ballot(lane < n_qtiles && g8 * c > s);
+  if (m == 0) return false;
+  t = __popcll(m) - 1;
+  const int i = s - g8 * (t + 1 < 64 ? __builtin_amdgcn_readlane(c, t + 1) : 0);
+  hl = i % g8;
+  const int k = i / g8;
+  const uint64_t m2 = __ballot(lane < batch && nt > t);
+  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m2 >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m2, 0u));
+  const uint64_t m3 = __ballot(((m2 >> lane) & 1ull) && rank == k);
+  b = m3 ? __ffsll((unsigned long long)m3) - 1 : -1;
+  return b >= 0;
+}
+
 // Largest grids (in 256-row workgroups) whose forward splits each row
 // group's keys between two waves: causal attention up to one round of the
 // CUs, full attention up to half of one (see the forward kernel). At head

@@ -108,16 +108,46 @@ void check_forward_d(const std::string& name, const Batch& x, int H, int Hkv, bo
   const int group = H / Hkv;
   std::vector<int> cover(rows_of(x, H), 0);
   const int64_t n_stat = rows_of(x, H);
-  for (int lin = 0; lin < (int)sh.grid; ++lin) {
-    int qt, p;
-    fa::fwd_tile_of(lin, sh.n_qtiles, bh_count, sh.pairs && !x.packed, qt, p);
-    CHECK(p >= 0 && p < bh_count && qt >= 0 && qt < sh.n_qtiles, "lin %d -> qt %d p %d", lin, qt,
-          p);
-    const int h = p / batch, b = p - h * batch, hk = h / group;
+  // Packed batches within the limits: only real tiles, heaviest first.
+  const bool lpt = x.packed && fa::fwd_packed_lpt_ok(batch, H, sh.n_qtiles);
+  const int64_t grid = lpt ? fa::fwd_packed_lpt_grid(batch, x.total, H, sh.bm, sh.n_qtiles)
+                           : sh.grid;
+  CHECK(grid <= sh.grid, "packed grid %lld above %lld", (long long)grid, (long long)sh.grid);
+  std::vector<int> last_t(8, 1 << 30);
+  std::vector<char> ended(8, 0);
+  for (int lin = 0; lin < (int)grid; ++lin) {
+    int qt, h, b;
+    if (lpt) {
+      const int g8 = H / 8, xcd = lin & 7;
+      int hl, t;
+      if (!fa::fwd_packed_lpt_host(x.cu.data(), batch, x.total, x.seqlen, sh.bm, sh.n_qtiles, g8,
+                                   lin >> 3, b, hl, t)) {
+        ended[xcd] = 1;
+        continue;
+      }
+      // Heaviest first: on each XCD the tile index never rises, and no
+      // slot after an empty one holds a tile.
+      CHECK(!ended[xcd] && t <= last_t[xcd], "lin %d: tile %d after %d", lin, t, last_t[xcd]);
+      last_t[xcd] = t;
+      CHECK(b >= 0 && b < batch && hl >= 0 && hl < g8 && t >= 0 && t < sh.n_qtiles,
+            "lin %d -> b %d hl %d t %d", lin, b, hl, t);
+      h = xcd * g8 + hl;
+      qt = t;
+    } else {
+      int p;
+      fa::fwd_tile_of(lin, sh.n_qtiles, bh_count, sh.pairs && !x.packed, qt, p);
+      CHECK(p >= 0 && p < bh_count && qt >= 0 && qt < sh.n_qtiles, "lin %d -> qt %d p %d", lin,
+            qt, p);
+      h = p / batch;
+      b = p - h * batch;
+    }
+    const int hk = h / group;
     int s0, n;
     span(x, b, s0, n);
-    qt = fa::fwd_seq_tile(qt, sh.n_qtiles, n, sh.bm, x.packed);
-    if (qt < 0) continue;
+    if (!lpt) {
+      qt = fa::fwd_seq_tile(qt, sh.n_qtiles, n, sh.bm, x.packed);
+      if (qt < 0) continue;
+    }
     const int q0 = qt * sh.bm;
     CHECK(q0 < n, "lin %d: tile %d starts past the sequence (%d rows)", lin, qt, n);
     for (int i = q0; i < q0 + sh.bm && i < n; ++i) {
@@ -137,8 +167,9 @@ void check_forward_d(const std::string& name, const Batch& x, int H, int Hkv, bo
   }
   std::string why;
   CHECK(exactly_once(x, H, cover, why), "%s", why.c_str());
-  std::printf("ok %s D%d: %lld workgroups, key split %d%s\n", name.c_str(), d,
-              (long long)sh.grid, sh.ks, sh.pairs && !x.packed ? ", pairwise order" : "");
+  std::printf("ok %s D%d: %lld workgroups, key split %d%s\n", name.c_str(), d, (long long)grid,
+              sh.ks,
+              lpt ? ", whole-batch order" : sh.pairs && !x.packed ? ", pairwise order" : "");
 }
 
 // Both head dims: their grid rules differ for the shortest grids.
@@ -155,14 +186,30 @@ void check_malformed(const std::string& name, const std::vector<int32_t>& cu, in
   const int batch = (int)x.lens.size();
   for (int d : {64, 128}) {
   const fa::FwdShape sh = fa::fwd_shape(batch * H, x.seqlen, causal, d);
-  for (int lin = 0; lin < (int)sh.grid; ++lin) {
-    int qt, p;
-    fa::fwd_tile_of(lin, sh.n_qtiles, batch * H, false, qt, p);
-    const int h = p / batch, b = p - h * batch;
+  const bool lpt = fa::fwd_packed_lpt_ok(batch, H, sh.n_qtiles);
+  const int64_t grid =
+      lpt ? fa::fwd_packed_lpt_grid(batch, x.total, H, sh.bm, sh.n_qtiles) : sh.grid;
+  for (int lin = 0; lin < (int)grid; ++lin) {
+    int qt, h, b;
+    if (lpt) {
+      int hl;
+      if (!fa::fwd_packed_lpt_host(x.cu.data(), batch, x.total, x.seqlen, sh.bm, sh.n_qtiles,
+                                   H / 8, lin >> 3, b, hl, qt))
+        continue;
+      CHECK(b >= 0 && b < batch && hl >= 0 && hl < H / 8, "malformed: b %d hl %d", b, hl);
+      h = (lin & 7) * (H / 8) + hl;
+    } else {
+      int p;
+      fa::fwd_tile_of(lin, sh.n_qtiles, batch * H, false, qt, p);
+      h = p / batch;
+      b = p - h * batch;
+    }
     int s0, n;
     span(x, b, s0, n);
-    qt = fa::fwd_seq_tile(qt, sh.n_qtiles, n, sh.bm, true);
-    if (qt < 0) continue;
+    if (!lpt) {
+      qt = fa::fwd_seq_tile(qt, sh.n_qtiles, n, sh.bm, true);
+      if (qt < 0) continue;
+    }
     for (int i = qt * sh.bm; i < qt * sh.bm + sh.bm && i < n; ++i) {
       CHECK(row_of(x, H, b, h, s0, i) < rows_of(x, H), "forward row out of bounds");
       CHECK(row_of(x, Hkv, b, h / (H / Hkv), s0, i) < rows_of(x, Hkv), "K/V row out of bounds");
@@ -375,11 +422,30 @@ int main() {
   check_forward("fwd packed empty first sequence", packed({0, 5}), 4, 4, true);
   check_backward("bwd packed empty first sequence", packed({0, 5}), 4, 4, true);
   check_forward("fwd packed 40 short", packed(std::vector<int>(40, 3)), 8, 2, true);
+  // The whole-batch order (heads a multiple of 8, at most 64 sequences and 64
+  // tiles): the edge lengths, with tokens after the last sequence, 64 and 65
+  // sequences (the second keeps the per-sequence order), a 64-tile sequence.
+  for (bool causal : {true, false})
+    for (int hkv : {8, 2, 1}) {
+      const std::string c = std::string(causal ? " causal" : " full") + " H8/" + std::to_string(hkv);
+      check_forward("fwd packed edge" + c, packed(edge), 8, hkv, causal);
+      check_forward("fwd packed edge + tail" + c, packed(edge, 37), 8, hkv, causal);
+    }
+  {
+    std::vector<int> many;
+    for (int i = 0; i < 65; ++i) many.push_back((i * 977) % 1500 + (i % 7 == 0 ? 0 : 1));
+    check_forward("fwd packed 65 sequences H16/4", packed(many), 16, 4, true);
+    many.pop_back();
+    check_forward("fwd packed 64 sequences H16/4", packed(many), 16, 4, true);
+    check_forward("fwd packed 64-tile sequence H8/8", packed({16384, 3, 1000}), 8, 8, true);
+    check_forward("fwd packed 65-tile sequence H8/8", packed({16385, 3, 1000}), 8, 8, false);
+  }
   // Malformed offsets: decreasing, negative, past the end.
   for (bool causal : {true, false}) {
     check_malformed("malformed offsets A", {0, 5, 3, 100}, 20, 4, 2, causal);
     check_malformed("malformed offsets B", {-7, 300, 250, 999, 1000}, 600, 4, 4, causal);
     check_malformed("malformed offsets C", {10, 2, 2000}, 512, 8, 1, causal);
+    check_malformed("malformed offsets D", {0, 900, 100, 100, 5000, 700}, 1000, 16, 4, causal);
   }
   // fp32 forward.
   for (int d : {64, 128}) {

@@ -148,3 +148,81 @@ def test_packed_large_grid_d64(causal):
                                        to64(v[s0:s1, hk])[None, None], 0.125, causal)
         assert_close(f"packed D64 seq {b} head {h}", to64(o[s0:s1, h])[None, None], ro, "bf16")
         assert_lse_close(f"packed D64 seq {b} head {h}", to64(lse[h, s0:s1])[None, None], rl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H_kv", [8, 2, 1])
+def test_whole_batch_order_every_row(D, causal, H_kv):
+    """Eight query heads take the grid of only real tiles, heaviest first over
+    the batch (with four heads above, the per-sequence order): every row of
+    every sequence against the oracle, from outputs filled with a sentinel so
+    that a tile left out or written twice elsewhere shows; the tokens after
+    the last sequence keep the sentinel."""
+    lengths = [1, 7, 0, 65, 300, 129, 256, 700]
+    q, k, v, cu = packed(lengths, 8, H_kv, D, "bf16", seed=4100 + D + H_kv + int(causal), extra=45)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((8, q.shape[0]), 7.0, dtype=torch.float32, device=DEV)
+    fa.forward_varlen(q, k, v, cu_t, max(lengths), causal=causal, scale=D ** -0.5, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_forward_varlen(to64(q), to64(k), to64(v), cu, D ** -0.5, causal)
+    n = cu[-1]
+    name = f"whole-batch order D{D} causal={causal} H8/{H_kv}"
+    assert_close(name + " O", to64(o)[:n], ro[:n], "bf16")
+    assert_lse_close(name, to64(lse)[:, :n], rl[:, :n])
+    assert bool((o[n:] == 7).all()) and bool((lse[:, n:] == 7).all())
+
+
+def test_whole_batch_order_matches_dense_bitwise():
+    """Equal lengths with eight heads (the whole-batch order) give the dense
+    entry point's results bit for bit."""
+    B, H, N, D = 3, 8, 700, 128
+    q, k, v = workloads.make_random((B, H, N, D), seed=57, dtype="bf16", device=DEV)
+    o, lse = fa.forward(q, k, v, causal=True, scale=0.1)
+    pk = [t.permute(0, 2, 1, 3).reshape(B * N, H, D).contiguous() for t in (q, k, v)]
+    cu = torch.tensor([0, N, 2 * N, 3 * N], dtype=torch.int32, device=DEV)
+    o2, lse2 = fa.forward_varlen(*pk, cu, N, causal=True, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o.permute(0, 2, 1, 3).reshape(B * N, H, D))
+    assert torch.equal(lse2, lse.permute(1, 0, 2).reshape(H, B * N))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_whole_batch_order_long_every_row(D, causal):
+    """The whole-batch order on the whole-key-range kernel (enough 256-row
+    tiles that keys are not split): every row against the oracle, sentinel
+    outputs as above."""
+    lengths = [1, 2000, 0, 3000, 777, 2500, 129]
+    q, k, v, cu = packed(lengths, 8, 2, D, "bf16", seed=4200 + D + int(causal), extra=11)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((8, q.shape[0]), 7.0, dtype=torch.float32, device=DEV)
+    fa.forward_varlen(q, k, v, cu_t, max(lengths), causal=causal, scale=D ** -0.5, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_forward_varlen(to64(q), to64(k), to64(v), cu, D ** -0.5, causal)
+    n = cu[-1]
+    name = f"whole-batch order, long, D{D} causal={causal} H8/2"
+    assert_close(name + " O", to64(o)[:n], ro[:n], "bf16")
+    assert_lse_close(name, to64(lse)[:, :n], rl[:, :n])
+    assert bool((o[n:] == 7).all()) and bool((lse[:, n:] == 7).all())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_whole_batch_order_four_way_split(causal):
+    """The whole-batch order on the D = 64 four-way key split (64-row tiles):
+    every row against the oracle, sentinel outputs as above."""
+    lengths = [1, 0, 500, 77]
+    q, k, v, cu = packed(lengths, 8, 2, 64, "bf16", seed=4300 + int(causal), extra=9)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((8, q.shape[0]), 7.0, dtype=torch.float32, device=DEV)
+    fa.forward_varlen(q, k, v, cu_t, max(lengths), causal=causal, scale=0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_forward_varlen(to64(q), to64(k), to64(v), cu, 0.125, causal)
+    n = cu[-1]
+    name = f"whole-batch order, four-way split, causal={causal}"
+    assert_close(name + " O", to64(o)[:n], ro[:n], "bf16")
+    assert_lse_close(name, to64(lse)[:, :n], rl[:, :n])
+    assert bool((o[n:] == 7).all()) and bool((lse[:, n:] == 7).all())

@@ -56,6 +56,12 @@ MUTANTS = {
                          "b = rest % n_splits;\n  split = rest / n_splits;"),
     "decode_chunk_round": ("chunk = (chunk + 127) / 128 * 128;", "chunk = chunk / 128 * 128;"),
     "decode_active_floor": ("const int n = (L + chunk - 1) / chunk;", "const int n = L / chunk;"),
+    "lpt_grid_bound": ("const int64_t bound = (total + batch * (bm - 1)) / bm;",
+                       "const int64_t bound = (total + bm - 1) / bm;"),
+    "lpt_tile_counts": ("c[l] += nt[j] - l > 0 ? nt[j] - l : 0;",
+                        "c[l] += nt[j] - l > 1 ? nt[j] - l : 0;"),
+    "lpt_rank": ("const int rank = __builtin_popcountll(m2 & ((1ull << l) - 1));",
+                 "const int rank = __builtin_popcountll(m2 & ((2ull << l) - 1));"),
     "split_rows": ("s.bm = 256 / s.ks;", "s.bm = 128;"),
     "f32_split_rows": ("s.bm = 32 * f32_row_groups(s.ks);", "s.bm = 32 * f32_row_groups(1);"),
 }
