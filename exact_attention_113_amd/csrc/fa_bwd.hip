@@ -231,7 +231,7 @@ __device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b, int h, in
 
 // ---------------------------------------------------------------- dK, dV
 
-template <typename TT, int D, bool DROP>
+template <typename TT, int D, bool DROP, bool COMPACT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams prm) {
   constexpr int BK = kBwdKeyTile;        // keys per workgroup: 32 per wave pair
   constexpr int BM = 64;                 // query rows per iteration
@@ -265,9 +265,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   // Q and dO in L2. Round-major (small grids): round r takes key tile r of
   // every unit, which spreads heavy and light tiles evenly over the CUs. The
   // group's query heads all contribute to this tile's dK and dV.
+  // COMPACT (packed batches within bwd_packed_compact_ok's limits): a grid
+  // of only real key tiles, in the unit-major order below.
   int unit, kt;
-  bwd_unit_slot(blockIdx.x, gridDim.x, prm.round_major != 0, prm.batch * (prm.heads / prm.group),
-                prm.n_tiles, unit, kt);
+  if constexpr (COMPACT) {
+    const int g8 = (prm.heads / prm.group) >> 3;
+    int j, b;
+    if (!bwd_packed_compact_wave(prm.cu, prm.batch, prm.total, prm.seqlen, BK, g8,
+                                 (int)(blockIdx.x >> 3), lane, j, b, kt))
+      return;  // past the batch's last key tile
+    unit = ((int)(blockIdx.x & 7) * g8 + j) * prm.batch + b;
+  } else {
+    bwd_unit_slot(blockIdx.x, gridDim.x, prm.round_major != 0, prm.batch * (prm.heads / prm.group),
+                  prm.n_tiles, unit, kt);
+  }
   const int hk = unit / prm.batch, bidx = unit - hk * prm.batch;
   const SeqRows sr0 = seq_rows<D>(prm, bidx, hk * prm.group, hk);
   const int N = sr0.N;
@@ -520,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 
 // ---------------------------------------------------------------- dQ
 
-template <typename TT, int D, bool DROP>
+template <typename TT, int D, bool DROP, bool COMPACT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm) {
   constexpr int BM = kBwdQueryTile;  // query rows per workgroup: 32 per wave
   static_assert(BM == 32 * kWaves, "one 32-row block per wave");
@@ -548,9 +559,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   // workgroups per CU): round r takes every unit's r-th tile counted back
   // from the end of its sequence, the forward's order, which pairs heavy and
   // light tiles on each CU exactly. Head h reads K/V head h / group.
+  // COMPACT: a grid of only real query tiles, in the unit-major order.
   int unit, round;
-  bwd_unit_slot(blockIdx.x, gridDim.x, prm.round_major != 0, prm.batch * prm.heads, prm.n_tiles,
-                unit, round);
+  if constexpr (COMPACT) {
+    const int g8 = prm.heads >> 3;
+    int j, b;
+    if (!bwd_packed_compact_wave(prm.cu, prm.batch, prm.total, prm.seqlen, BM, g8,
+                                 (int)(blockIdx.x >> 3), lane, j, b, round))
+      return;  // past the batch's last query tile
+    unit = ((int)(blockIdx.x & 7) * g8 + j) * prm.batch + b;
+  } else {
+    bwd_unit_slot(blockIdx.x, gridDim.x, prm.round_major != 0, prm.batch * prm.heads, prm.n_tiles,
+                  unit, round);
+  }
   const int h = unit / prm.batch, bidx = unit - h * prm.batch;
   const int bh = bidx * prm.heads + h;
   const SeqRows sr = seq_rows<D>(prm, bidx, h, h / prm.group);
@@ -558,7 +579,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   // Unit-major counts from the longest sequence's end (its empty slots
   // then sit at the start of the unit's range), round-major from this
   // sequence's own end.
-  const int qt = bwd_dq_tile(round, prm.round_major != 0, prm.n_tiles, N, BM);
+  // (The compact order's rank r is query tile n_b - 1 - r of its unit.)
+  const int qt = COMPACT ? (N + BM - 1) / BM - 1 - round
+                         : bwd_dq_tile(round, prm.round_major != 0, prm.n_tiles, N, BM);
   if (qt < 0) return;  // a slot past the end of a shorter sequence
   const int q0 = qt * BM;
   LdsOffsets<D> ldo;
@@ -747,21 +770,33 @@ hipError_t launch_typed(const BwdArgs& a, const BwdWorkspace& ws) {
 
   // Grids and work orders (round-major for small causal grids): bwd_shape.
   const BwdShape sh = bwd_shape(a.B, a.H, hkv, a.N, a.causal != 0);
-  const dim3 g1((unsigned)sh.grid_dkdv);
-  const dim3 g2((unsigned)sh.grid_dq);
+  // Packed batches: grids of only real tiles where the limits allow.
+  const bool c1 = packed && bwd_packed_compact_ok(a.B, hkv, sh.rm_dkdv);
+  const bool c2 = packed && bwd_packed_compact_ok(a.B, a.H, sh.rm_dq);
+  const dim3 g1((unsigned)(c1 ? bwd_packed_compact_grid(a.B, a.total, hkv, kBwdKeyTile, sh.n_ktiles)
+                              : sh.grid_dkdv));
+  const dim3 g2((unsigned)(c2 ? bwd_packed_compact_grid(a.B, a.total, a.H, kBwdQueryTile,
+                                                        sh.n_qtiles)
+                              : sh.grid_dq));
   prm.diag = a.causal ? 0 : (int)a.N;
   auto go = [&](auto drop) -> hipError_t {
     constexpr bool DR = decltype(drop)::value;
     BwdParams p1 = prm;
     p1.n_tiles = sh.n_ktiles;
     p1.round_major = sh.rm_dkdv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR>), g1, dim3(kThreads), 0, a.stream, p1);
+    if (c1)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR, true>), g1, dim3(kThreads), 0, a.stream, p1);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DR, false>), g1, dim3(kThreads), 0, a.stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     BwdParams p2 = prm;
     p2.n_tiles = sh.n_qtiles;
     p2.round_major = sh.rm_dq;
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR>), g2, dim3(kThreads), 0, a.stream, p2);
+    if (c2)
+      hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR, true>), g2, dim3(kThreads), 0, a.stream, p2);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DR, false>), g2, dim3(kThreads), 0, a.stream, p2);
     return hipGetLastError();
   };
   using T_ = std::true_type;

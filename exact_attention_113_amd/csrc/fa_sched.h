@@ -267,6 +267,67 @@ __host__ __device__ inline int bwd_dq_tile(int slot, bool round_major, int n_til
   return (qt < 0 || qt * bm >= n) ? -1 : qt;
 }
 
+// Packed backward grids in the unit-major order (each XCD works through
+// the units of its heads one after another, sequences in order, a unit's
+// tiles heaviest first) hold only the batch's real tiles: the workgroups
+// that the grid sized by the longest sequence gives each shorter sequence's
+// unit past its end, and that exit at once, are left out. The units are
+// (sequence, head) with `heads` the K/V heads (dK/dV) or the query heads
+// (dQ); XCD x owns heads x * heads/8 .. + heads/8 - 1. Slot s of an XCD
+// gives its head j, the sequence b and r, the rank of the tile within the
+// unit in the order above (dK/dV: key tile r; dQ: query tile n_b - 1 - r).
+// The device form keeps one sequence per lane, hence the limit.
+inline bool bwd_packed_compact_ok(int64_t batch, int64_t heads, bool round_major) {
+  return !round_major && heads % 8 == 0 && batch <= kLptMaxBatch;
+}
+inline int64_t bwd_packed_compact_grid(int64_t batch, int64_t total, int64_t heads, int bt,
+                                       int n_tiles) {
+  const int64_t bound = (total + batch * (bt - 1)) / bt;
+  const int64_t most = batch * (int64_t)n_tiles;
+  return heads * (bound < most ? bound : most);
+}
+// Host form, the device form's steps over the lanes one after another
+// (lane j: sequence j's tile count and the tiles of the sequences before it).
+inline bool bwd_packed_compact_host(const int32_t* cu, int batch, int total, int seqlen, int bt,
+                                    int g8, int s, int& j, int& b, int& r) {
+  int nt[64], pre[64], sum = 0;
+  for (int l = 0; l < 64; ++l) {
+    nt[l] = l < batch ? packed_tiles(cu, l, total, seqlen, bt) : 0;
+    pre[l] = sum;
+    sum += nt[l];
+  }
+  if (sum == 0) return false;
+  j = s / sum;
+  if (j >= g8) return false;
+  const int rr = s - j * sum;
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l) m |= (uint64_t)(l < batch && pre[l] <= rr && rr < pre[l] + nt[l]) << l;
+  if (m == 0) return false;
+  b = __builtin_ctzll(m);
+  r = rr - pre[b];
+  return true;
+}
+__device__ inline bool bwd_packed_compact_wave(const int32_t* cu, int batch, int total, int seqlen,
+                                               int bt, int g8, int s, int lane, int& j, int& b,
+                                               int& r) {
+  const int nt = lane < batch ? packed_tiles(cu, lane, total, seqlen, bt) : 0;
+  int pre = 0, sum = 0;
+  for (int l = 0; l < batch; ++l) {
+    const int x = __builtin_amdgcn_readlane(nt, l);
+    pre += l < lane ? x : 0;
+    sum += x;
+  }
+  if (sum == 0) return false;
+  j = s / sum;
+  if (j >= g8) return false;
+  const int rr = s - j * sum;
+  const uint64_t m = __ballot(lane < batch && pre <= rr && rr < pre + nt);
+  if (m == 0) return false;
+  b = __ffsll((unsigned long long)m) - 1;
+  r = rr - __builtin_amdgcn_readlane(pre, b);
+  return true;
+}
+
 constexpr int kBwdKeyTile = 128;    // keys per dK/dV workgroup
 constexpr int kBwdQueryTile = 256;  // query rows per dQ workgroup
 // Causal dQ grids of at most two workgroups per CU run round-major

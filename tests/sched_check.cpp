@@ -262,6 +262,8 @@ void check_forward_f32(const std::string& name, int B, int H, int N, int D) {
 
 // Backward: dK/dV over key tiles of each (sequence, K/V head), dQ over query
 // tiles of each (sequence, query head).
+int units_q_of(int batch, int H) { return batch * H; }
+
 void check_backward(const std::string& name, const Batch& x, int H, int Hkv, bool causal) {
   ++g_cases;
   const int batch = (int)x.lens.size();
@@ -270,9 +272,43 @@ void check_backward(const std::string& name, const Batch& x, int H, int Hkv, boo
   std::vector<int> cover_kv(rows_of(x, Hkv), 0), cover_q(rows_of(x, H), 0);
   const int64_t n_stat = rows_of(x, H);
   const int units_kv = batch * Hkv;
-  for (int blk = 0; blk < (int)sh.grid_dkdv; ++blk) {
+  // Packed grids within the limits hold only real tiles: each XCD's list of
+  // (unit, tile) must be the full grid's list with the empty slots left out.
+  const bool c1 = x.packed && fa::bwd_packed_compact_ok(batch, Hkv, sh.rm_dkdv);
+  const bool c2 = x.packed && fa::bwd_packed_compact_ok(batch, H, sh.rm_dq);
+  std::vector<std::vector<std::pair<int, int>>> full_kv(8), compact_kv(8), full_q(8), compact_q(8);
+  if (c1)
+    for (int blk = 0; blk < (int)sh.grid_dkdv; ++blk) {
+      int unit, kt, s0, n;
+      fa::bwd_unit_slot(blk, (int)sh.grid_dkdv, false, units_kv, sh.n_ktiles, unit, kt);
+      span(x, unit % batch, s0, n);
+      if (kt * fa::kBwdKeyTile < n) full_kv[blk & 7].push_back({unit, kt});
+    }
+  if (c2)
+    for (int blk = 0; blk < (int)sh.grid_dq; ++blk) {
+      int unit, slot, s0, n;
+      fa::bwd_unit_slot(blk, (int)sh.grid_dq, false, units_q_of(batch, H), sh.n_qtiles, unit, slot);
+      span(x, unit % batch, s0, n);
+      const int qt = fa::bwd_dq_tile(slot, false, sh.n_qtiles, n, fa::kBwdQueryTile);
+      if (qt >= 0) full_q[blk & 7].push_back({unit, qt});
+    }
+  const int64_t grid1 =
+      c1 ? fa::bwd_packed_compact_grid(batch, x.total, Hkv, fa::kBwdKeyTile, sh.n_ktiles)
+         : sh.grid_dkdv;
+  CHECK(grid1 <= sh.grid_dkdv, "compact dK/dV grid above the full one");
+  for (int blk = 0; blk < (int)grid1; ++blk) {
     int unit, kt;
-    fa::bwd_unit_slot(blk, (int)sh.grid_dkdv, sh.rm_dkdv, units_kv, sh.n_ktiles, unit, kt);
+    if (c1) {
+      const int g8 = Hkv / 8;
+      int j, bb;
+      if (!fa::bwd_packed_compact_host(x.cu.data(), batch, x.total, x.seqlen, fa::kBwdKeyTile, g8,
+                                       blk >> 3, j, bb, kt))
+        continue;
+      unit = ((blk & 7) * g8 + j) * batch + bb;
+      compact_kv[blk & 7].push_back({unit, kt});
+    } else {
+      fa::bwd_unit_slot(blk, (int)sh.grid_dkdv, sh.rm_dkdv, units_kv, sh.n_ktiles, unit, kt);
+    }
     CHECK(unit >= 0 && unit < units_kv && kt >= 0 && kt < sh.n_ktiles, "dK/dV blk %d", blk);
     const int hk = unit / batch, b = unit - hk * batch;
     int s0, n;
@@ -292,14 +328,34 @@ void check_backward(const std::string& name, const Batch& x, int H, int Hkv, boo
       }
   }
   const int units_q = batch * H;
-  for (int blk = 0; blk < (int)sh.grid_dq; ++blk) {
-    int unit, slot;
-    fa::bwd_unit_slot(blk, (int)sh.grid_dq, sh.rm_dq, units_q, sh.n_qtiles, unit, slot);
-    CHECK(unit >= 0 && unit < units_q && slot >= 0 && slot < sh.n_qtiles, "dQ blk %d", blk);
-    const int h = unit / batch, b = unit - h * batch;
-    int s0, n;
-    span(x, b, s0, n);
-    const int qt = fa::bwd_dq_tile(slot, sh.rm_dq, sh.n_qtiles, n, fa::kBwdQueryTile);
+  const int64_t grid2 =
+      c2 ? fa::bwd_packed_compact_grid(batch, x.total, H, fa::kBwdQueryTile, sh.n_qtiles)
+         : sh.grid_dq;
+  CHECK(grid2 <= sh.grid_dq, "compact dQ grid above the full one");
+  for (int blk = 0; blk < (int)grid2; ++blk) {
+    int unit, h, b, s0, n, qt;
+    if (c2) {
+      const int g8 = H / 8;
+      int j, r;
+      if (!fa::bwd_packed_compact_host(x.cu.data(), batch, x.total, x.seqlen, fa::kBwdQueryTile,
+                                       g8, blk >> 3, j, b, r))
+        continue;
+      unit = ((blk & 7) * g8 + j) * batch + b;
+      CHECK(unit >= 0 && unit < units_q, "dQ blk %d", blk);
+      h = unit / batch;
+      span(x, b, s0, n);
+      qt = (n + fa::kBwdQueryTile - 1) / fa::kBwdQueryTile - 1 - r;
+      CHECK(qt >= 0, "dQ blk %d: rank %d past the sequence", blk, r);
+      compact_q[blk & 7].push_back({unit, qt});
+    } else {
+      int slot;
+      fa::bwd_unit_slot(blk, (int)sh.grid_dq, sh.rm_dq, units_q, sh.n_qtiles, unit, slot);
+      CHECK(unit >= 0 && unit < units_q && slot >= 0 && slot < sh.n_qtiles, "dQ blk %d", blk);
+      h = unit / batch;
+      b = unit - h * batch;
+      span(x, b, s0, n);
+      qt = fa::bwd_dq_tile(slot, sh.rm_dq, sh.n_qtiles, n, fa::kBwdQueryTile);
+    }
     if (qt < 0) continue;
     const int q0 = qt * fa::kBwdQueryTile;
     CHECK(q0 < n, "dQ blk %d: tile %d starts past the sequence (%d rows)", blk, qt, n);
@@ -310,12 +366,17 @@ void check_backward(const std::string& name, const Batch& x, int H, int Hkv, boo
       ++cover_q[r];
     }
   }
+  for (int xcd = 0; xcd < 8; ++xcd) {
+    CHECK(!c1 || compact_kv[xcd] == full_kv[xcd], "dK/dV XCD %d: compact order differs", xcd);
+    CHECK(!c2 || compact_q[xcd] == full_q[xcd], "dQ XCD %d: compact order differs", xcd);
+  }
   std::string why;
   CHECK(exactly_once(x, Hkv, cover_kv, why), "dK/dV: %s", why.c_str());
   CHECK(exactly_once(x, H, cover_q, why), "dQ: %s", why.c_str());
   std::printf("ok %s: dK/dV %lld workgroups (%s), dQ %lld (%s)\n", name.c_str(),
-              (long long)sh.grid_dkdv, sh.rm_dkdv ? "round-major" : "unit-major",
-              (long long)sh.grid_dq, sh.rm_dq ? "round-major" : "unit-major");
+              (long long)grid1,
+              c1 ? "real tiles only" : sh.rm_dkdv ? "round-major" : "unit-major",
+              (long long)grid2, c2 ? "real tiles only" : sh.rm_dq ? "round-major" : "unit-major");
 }
 
 // Decode: chunks of the cache of each (sequence, K/V head).
@@ -430,7 +491,22 @@ int main() {
       const std::string c = std::string(causal ? " causal" : " full") + " H8/" + std::to_string(hkv);
       check_forward("fwd packed edge" + c, packed(edge), 8, hkv, causal);
       check_forward("fwd packed edge + tail" + c, packed(edge, 37), 8, hkv, causal);
+      check_backward("bwd packed edge" + c, packed(edge), 8, hkv, causal);
+      check_backward("bwd packed edge + tail" + c, packed(edge, 37), 8, hkv, causal);
     }
+  // Backward grids of only real tiles (unit-major grids, K/V or query heads
+  // a multiple of 8): the prefill lengths with H16/8 and H8/8, 64 and 65
+  // sequences.
+  for (bool causal : {true, false}) {
+    const std::string c = causal ? " causal" : " full";
+    check_backward("bwd packed prefill H16/8" + c, packed(prefill), 16, 8, causal);
+    check_backward("bwd packed prefill + tail H8/8" + c, packed(prefill, 300), 8, 8, causal);
+    std::vector<int> many;
+    for (int i = 0; i < 65; ++i) many.push_back((i * 613) % 900 + (i % 9 == 0 ? 0 : 2));
+    check_backward("bwd packed 65 sequences H8/8" + c, packed(many), 8, 8, causal);
+    many.pop_back();
+    check_backward("bwd packed 64 sequences H8/8" + c, packed(many), 8, 8, causal);
+  }
   {
     std::vector<int> many;
     for (int i = 0; i < 65; ++i) many.push_back((i * 977) % 1500 + (i % 7 == 0 ? 0 : 1));

@@ -62,6 +62,10 @@ MUTANTS = {
                         "c[l] += nt[j] - l > 1 ? nt[j] - l : 0;"),
     "lpt_rank": ("const int rank = __builtin_popcountll(m2 & ((1ull << l) - 1));",
                  "const int rank = __builtin_popcountll(m2 & ((2ull << l) - 1));"),
+    "compact_grid_bound": ("const int64_t bound = (total + batch * (bt - 1)) / bt;",
+                           "const int64_t bound = (total + bt - 1) / bt;"),
+    "compact_prefix_inclusive": ("pre[l] = sum;\n    sum += nt[l];",
+                                 "sum += nt[l];\n    pre[l] = sum;"),
     "split_rows": ("s.bm = 256 / s.ks;", "s.bm = 128;"),
     "f32_split_rows": ("s.bm = 32 * f32_row_groups(s.ks);", "s.bm = 32 * f32_row_groups(1);"),
 }
