@@ -100,7 +100,7 @@ struct DecParams {
   const int32_t* seqlens;   // [B] cached tokens per sequence
   float* part_o;            // [B, H, s_q, n_splits, D] (split mode)
   float* part_lse;          // [B, H, s_q, n_splits]    (split mode)
-  int s_q, cap, max_len, heads, hkv, group, n_splits, chunk;
+  int batch, s_q, cap, max_len, heads, hkv, group, n_splits, chunk;
   float c;                  // |scale| * log2(e)
   uint32_t qsign;           // sign flip of Q for a negative scale
 };
@@ -129,7 +129,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecParams 
   const int lq = lane & 31, hi = lane >> 5;
 
   int b, hk, split;
-  decode_unit(blockIdx.x, prm.n_splits, prm.hkv, b, hk, split);
+  if (prm.batch <= kDecodeOrderMaxBatch) {
+    // Active chunks first (decode_active_unit_wave); past them, nothing to do.
+    hk = (int)(blockIdx.x % prm.hkv);
+    if (!decode_active_unit_wave(prm.seqlens, prm.batch, prm.max_len, prm.chunk, prm.n_splits,
+                                 (int)(blockIdx.x / prm.hkv), lane, b, split))
+      return;
+  } else {
+    decode_unit(blockIdx.x, prm.n_splits, prm.hkv, b, hk, split);
+  }
   const int L = min(max(prm.seqlens[b], 0), prm.max_len);
   const int k_lo = split * prm.chunk;
   const int k_hi = min(L, k_lo + prm.chunk);
@@ -420,7 +428,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode16_kernel(const DecParam
   const int q = lane & 15, g = lane >> 4;
 
   int b, hk, split;
-  decode_unit(blockIdx.x, prm.n_splits, prm.hkv, b, hk, split);
+  if (prm.batch <= kDecodeOrderMaxBatch) {
+    // Active chunks first (decode_active_unit_wave); past them, nothing to do.
+    hk = (int)(blockIdx.x % prm.hkv);
+    if (!decode_active_unit_wave(prm.seqlens, prm.batch, prm.max_len, prm.chunk, prm.n_splits,
+                                 (int)(blockIdx.x / prm.hkv), lane, b, split))
+      return;
+  } else {
+    decode_unit(blockIdx.x, prm.n_splits, prm.hkv, b, hk, split);
+  }
   const int L = min(max(prm.seqlens[b], 0), prm.max_len);
   const int k_lo = split * prm.chunk;
   const int k_hi = min(L, k_lo + prm.chunk);
@@ -749,6 +765,7 @@ hipError_t launch_typed(const DecodeArgs& a, const DecodePlan& plan) {
   p.seqlens = a.cache_seqlens;
   p.part_o = plan.n_splits > 1 ? (float*)((char*)a.workspace + plan.part_o_off) : nullptr;
   p.part_lse = plan.n_splits > 1 ? (float*)((char*)a.workspace + plan.part_lse_off) : nullptr;
+  p.batch = (int)a.B;
   p.s_q = (int)a.s_q;
   p.cap = (int)a.cap;
   p.max_len = (int)a.max_len;

@@ -381,6 +381,49 @@ __host__ __device__ inline int decode_active_chunks(int L, int chunk, int n_spli
   return n < n_splits ? n : n_splits;
 }
 
+// Batches of at most kDecodeOrderMaxBatch sequences number the chunks that
+// hold keys first: workgroup blk takes K/V head blk % H_kv (heads fastest, as
+// above) of active chunk c = blk / H_kv, the chunks of sequence 0 first, then
+// sequence 1's, and so on; the workgroups past the last active chunk exit
+// after all real work has been dispatched instead of holding CUs among it.
+// The device form keeps one sequence per lane.
+constexpr int kDecodeOrderMaxBatch = 64;
+__host__ __device__ inline int decode_active_of(const int32_t* seqlens, int b, int max_len,
+                                                int chunk, int n_splits) {
+  const int L0 = seqlens[b];
+  const int L = L0 < 0 ? 0 : (L0 > max_len ? max_len : L0);
+  return decode_active_chunks(L, chunk, n_splits);
+}
+inline bool decode_active_unit_host(const int32_t* seqlens, int batch, int max_len, int chunk,
+                                    int n_splits, int c, int& b, int& split) {
+  int pre = 0;
+  for (int l = 0; l < batch; ++l) {
+    const int na = decode_active_of(seqlens, l, max_len, chunk, n_splits);
+    if (c < pre + na) {
+      b = l;
+      split = c - pre;
+      return true;
+    }
+    pre += na;
+  }
+  return false;
+}
+__device__ inline bool decode_active_unit_wave(const int32_t* seqlens, int batch, int max_len,
+                                               int chunk, int n_splits, int c, int lane, int& b,
+                                               int& split) {
+  const int na = lane < batch ? decode_active_of(seqlens, lane, max_len, chunk, n_splits) : 0;
+  int pre = 0;
+  for (int l = 0; l < batch; ++l) {
+    const int x = __builtin_amdgcn_readlane(na, l);
+    pre += l < lane ? x : 0;
+  }
+  const uint64_t m = __ballot(lane < batch && pre <= c && c < pre + na);
+  if (m == 0) return false;
+  b = __ffsll((unsigned long long)m) - 1;
+  split = c - __builtin_amdgcn_readlane(pre, b);
+  return true;
+}
+
 // Workgroups the chunk plan aims for, and the most chunks per row (one
 // lane of the merge kernel's wave each).
 #ifndef FA_DECODE_TARGET_WGS

@@ -394,9 +394,23 @@ void check_decode(const std::string& name, int s_q, int H, int Hkv, int cap, int
   const int group = H / Hkv;
   std::vector<int> cover((size_t)B * Hkv * cap, 0);
   std::vector<int> written((size_t)B * Hkv * plan.n_splits, 0);
+  // Batches within the limit number the active chunks first (heads fastest);
+  // no workgroup after the first that exits has work.
+  const bool ordered = B <= fa::kDecodeOrderMaxBatch;
+  bool exited = false;
   for (int blk = 0; blk < grid; ++blk) {
     int b, hk, split;
-    fa::decode_unit(blk, plan.n_splits, Hkv, b, hk, split);
+    if (ordered) {
+      hk = blk % Hkv;
+      if (!fa::decode_active_unit_host(lens.data(), B, max_len, plan.chunk, plan.n_splits,
+                                       blk / Hkv, b, split)) {
+        exited = true;
+        continue;
+      }
+      CHECK(!exited, "blk %d has work after an idle workgroup", blk);
+    } else {
+      fa::decode_unit(blk, plan.n_splits, Hkv, b, hk, split);
+    }
     CHECK(b >= 0 && b < B && hk >= 0 && hk < Hkv && split >= 0 && split < plan.n_splits,
           "blk %d", blk);
     const int L = std::min(std::max(lens[b], 0), max_len);
@@ -558,6 +572,14 @@ int main() {
     }
   check_decode("decode short caches", 1, 64, 32, 100, 100, {1, 50, 100, 7});
   check_decode("decode empty bound", 1, 4, 4, 64, 0, {0, 3});
+  {
+    // 64 sequences take the active-first order, 65 the plain one.
+    std::vector<int> many;
+    for (int i = 0; i < 65; ++i) many.push_back((i * 331) % 3000 - (i % 11 == 0 ? 50 : 0));
+    check_decode("decode 65 sequences", 1, 8, 2, 3000, 3000, many);
+    many.pop_back();
+    check_decode("decode 64 sequences", 2, 8, 2, 3000, 2900, many);
+  }
   std::printf("%d cases, %d failed\n", g_cases, g_fail);
   return g_fail ? 1 : 0;
 }

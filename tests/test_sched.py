@@ -66,6 +66,7 @@ MUTANTS = {
                            "const int64_t bound = (total + bt - 1) / bt;"),
     "compact_prefix_inclusive": ("pre[l] = sum;\n    sum += nt[l];",
                                  "sum += nt[l];\n    pre[l] = sum;"),
+    "decode_order_off_by_one": ("    if (c < pre + na) {", "    if (c <= pre + na) {"),
     "split_rows": ("s.bm = 256 / s.ks;", "s.bm = 128;"),
     "f32_split_rows": ("s.bm = 32 * f32_row_groups(s.ks);", "s.bm = 32 * f32_row_groups(1);"),
 }
