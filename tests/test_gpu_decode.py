@@ -106,3 +106,19 @@ def test_decode_repeatable_and_workspace_reuse():
     o2, l2 = fa.decode(q, k, v, lt, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("B", [64, 65])
+def test_decode_many_sequences_chunked(B):
+    """64 sequences take the order that numbers the chunks holding keys
+    first, 65 the plain one; caches of 0..700 tokens in 128-key chunks,
+    every row against the oracle."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1000 + B)
+    lens = [int(x) for x in torch.randint(0, 701, (B,), generator=g)]
+    lens[3] = 0
+    q, k, v = cache_inputs(B, 700, 1, 8, 2, 128, "bf16", seed=1100 + B)
+    assert fa.decode_workspace_bytes(B, 1, 8, 2, 700, 128) > 0
+    o, lse = fa.decode(q, k, v, torch.tensor(lens, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    check(f"{B} sequences chunked", o, lse, q, k, v, lens, 128 ** -0.5, "bf16")

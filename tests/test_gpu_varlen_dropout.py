@@ -98,3 +98,49 @@ def test_equal_lengths_match_dense_dropout_bitwise():
     assert torch.equal(lp, lse.permute(1, 0, 2).reshape(H, B * N))
     for a, b in zip(gp, g):
         assert torch.equal(a, pk(b))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H_kv", [8, 2])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_dropout_whole_batch_order(D, H_kv, causal):
+    """Eight query heads: the forward's grid of only real tiles, heaviest
+    first over the batch, and (full attention, unit-major grids) the
+    backward's grids of only real tiles, with dropout."""
+    lengths = [1, 7, 0, 65, 300, 129, 700]
+    q, k, v, do, cu = packed(lengths, 8, H_kv, D, seed=820 + D + H_kv + int(causal))
+    scale = D ** -0.5
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    kw = dict(causal=causal, scale=scale, dropout_p=P, seed=SEED, offset=OFFSET)
+    o, lse = fa.forward_varlen(q, k, v, cu_t, max(lengths), **kw)
+    dq, dk, dv = fa.backward_varlen(q, k, v, o, lse, do, cu_t, max(lengths), **kw)
+    torch.cuda.synchronize()
+    ro, rl, rq, rk, rv = oracle(q, k, v, do, cu, scale, causal)
+    name = f"packed dropout D{D} H8/{H_kv} causal={causal}"
+    assert_close(name + " O", to64(o), ro, "bf16")
+    assert_lse_close(name, to64(lse), rl)
+    assert_close(name + " dQ", to64(dq), rq, "bf16")
+    assert_close(name + " dK", to64(dk), rk, "bf16")
+    assert_close(name + " dV", to64(dv), rv, "bf16")
+
+
+def test_equal_lengths_match_dense_dropout_bitwise_eight_heads():
+    """The same with eight heads and full attention, where the packed grids
+    hold only real tiles (forward and both backward kernels)."""
+    B, H, N, D = 2, 8, 600, 128
+    q, k, v = workloads.make_random((B, H, N, D), seed=63, dtype="bf16", device=DEV)
+    do = workloads.make_random((B, H, N, D), seed=64, dtype="bf16", count=1, device=DEV)[0]
+    kw = dict(causal=False, scale=D ** -0.5, dropout_p=P, seed=SEED, offset=OFFSET)
+    o, lse = fa.forward(q, k, v, **kw)
+    g = fa.backward(q, k, v, o, lse, do, **kw)
+
+    def pk(t):
+        return t.permute(0, 2, 1, 3).reshape(B * N, H, D).contiguous()
+    cu = torch.tensor([0, N, 2 * N], dtype=torch.int32, device=DEV)
+    op, lp = fa.forward_varlen(pk(q), pk(k), pk(v), cu, N, **kw)
+    gp = fa.backward_varlen(pk(q), pk(k), pk(v), op, lp, pk(do), cu, N, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(op, pk(o))
+    assert torch.equal(lp, lse.permute(1, 0, 2).reshape(H, B * N))
+    for a, b in zip(gp, g):
+        assert torch.equal(a, pk(b))
