@@ -21,9 +21,9 @@ constexpr float kTau = 8.0f;
 // 32 keys, and wave kh of the group computes block kh of every tile with
 // its own online-softmax state. At the end the KS states of a row group are
 // merged (the rescale-and-add of the online softmax over disjoint key
-// sets). KS = 1 is the plain kernel (four waves over whole key ranges);
-// small grids use KS times more waves per query row and a KS times shorter
-// key loop per wave.
+// sets). Every workgroup has four waves: KS = 1 is the plain kernel (four
+// row groups over whole key ranges); small grids use KS waves per row group
+// (4 / KS row groups) and a KS times shorter key loop per wave.
 template <int D, bool CAUSAL, int KS>
 __global__ __launch_bounds__(64 * f32_row_groups(KS) * KS, 1) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
