@@ -3,7 +3,9 @@
 // kernel cuts a cache into chunks. Host and device code share these
 // functions, so the mapping the kernels run is the one the CPU-side
 // coverage check enumerates (every row produced exactly once, every index
-// inside its tensor).
+// inside its tensor). The orders a wave computes with one sequence per lane
+// (`*_wave`) have a host form (`*_host`) that runs the same steps lane by
+// lane; the check enumerates that.
 #pragma once
 
 #include <hip/hip_runtime.h>
