@@ -97,18 +97,16 @@ def test_repeatable_and_offset_changes_bits():
 
 @pytest.mark.timeout(900)
 def test_training_shape_heads():
-    """The training shape (B4 H16 N8192 D128 causal) with p = 0.1: eight
-    heads, one in each XCD's range of the head-major work order and at a
-    different position in it, forward and gradients against the oracle at
-    full length."""
+    """The training shape (B4 H16 N8192 D128 causal) with p = 0.1: every one
+    of the 64 heads, forward and gradients against the oracle at full
+    length."""
     w = workloads.bf16_training()
     q, k, v, do = workloads.make_inputs(w, device=DEV)
     kw = dict(causal=True, scale=w.scale, dropout_p=0.1, seed=2024, offset=7)
     o, lse = fa.forward(q, k, v, **kw)
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, **kw)
     torch.cuda.synchronize()
-    # Work item p = h * B + b; XCD x takes p in [8x, 8x + 8).
-    heads = [((9 * x) % w.B, (9 * x) // w.B) for x in range(8)]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
     def fwd(q1, k1, v1, head):
         return orc.attention_forward_dropout(q1, k1, v1, w.scale, True, 0.1, 2024, 7,
