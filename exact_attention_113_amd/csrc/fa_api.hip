@@ -182,6 +182,8 @@ fa_status drop_params(float p, uint64_t seed, uint64_t offset, int dtype, const 
   out->k1 = (uint32_t)(seed >> 32);
   out->offset = (uint32_t)offset;
   out->inv_keep = (float)(1.0 / (1.0 - thr / 256.0));
+  out->thr4 = thr * 0x01010101u;
+  out->bias4 = 0x80808080u - (out->thr4 & 0x7f7f7f7fu);
   return FA_OK;
 }
 

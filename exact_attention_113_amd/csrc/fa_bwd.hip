@@ -247,6 +247,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   __shared__ __attribute__((aligned(16))) float st1[2 * BM];
   // P of each pair: [pair][q-block][4 x u32x4 per lane][64 lanes], fp32.
   __shared__ __attribute__((aligned(16))) f32x4 pex[4 * 2 * 4 * 64];
+  // With dropout, the keep flags of each pair's scores (role B computes
+  // them, role A masks its dV operand with them): [pair][q-block][64 lanes].
+  __shared__ __attribute__((aligned(16))) u32x4 kex[DROP ? 4 * 2 * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -376,42 +379,46 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
         p[r] = x;
       }
     }
-    // With dropout, P goes to the partner with its sign bit set where the
-    // element is dropped (P >= 0, so the bit is free), and the dV operand
-    // holds the kept probabilities (dV is scaled by 1 / (1 - p) at the end).
-    float pd[16];
-    if constexpr (DROP) {
-      const uint32_t bits =
-          keep_bits_keys(drop, bidx * prm.heads + h, key, i * BM + 32 * qb, hi, lane & 3);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool kept = (bits >> r) & 1u;
-        pd[r] = kept ? p[r] : 0.f;
-        p[r] = kept ? p[r] : -p[r];  // sign bit set (-0 for a masked 0)
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pd[r] = p[r];
-    }
+    // P goes to the partner unmasked; with dropout the dV operand is masked
+    // after the barrier, with the keep flags the partner computed meanwhile.
     f32x4* dst = pex + ((pair * 2 + qb) * 4) * 64 + lane;
 #pragma unroll
     for (int m = 0; m < 4; ++m) dst[64 * m] = f32x4{p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pp[h][e] = TT::pack2(pd[8 * h + 2 * e], pd[8 * h + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) pp[h][e] = TT::pack2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
   };
 
   // Role B, phase 1: dP = dO V^T for one query block.
-  auto phase_b1 = [&] __device__ (const char* gt, int qb, f32x16& dp) __attribute__((always_inline)) {
+  // With dropout, also the keep flags of the block (lane = key, register =
+  // row, the layout of S and dP), kept for phase 2 and shared with role A:
+  // Philox work that overlaps this role's products instead of lengthening
+  // role A's phase 1, which the barrier waits for.
+  auto phase_b1 = [&] __device__ (const char* gt, int qb, f32x16& dp, int i, int h, u32x4& kf)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(gt, 32 * qb, ldo, kk), bf[kk], dp);
+    if constexpr (DROP) {
+      kf = keep_flags_keys(drop, bidx * prm.heads + h, key, i * BM + 32 * qb, hi, lane & 3);
+      kex[(pair * 2 + qb) * 64 + lane] = kf;
+    }
   };
 
   // Role A, phase 2: dV^T += dO^T P.
-  auto phase_a2 = [&] __device__ (const char* gt, int qb, const u32x4 (&pp)[2]) __attribute__((always_inline)) {
+  auto phase_a2 = [&] __device__ (const char* gt, int qb, const u32x4 (&pp0)[2]) __attribute__((always_inline)) {
+    u32x4 pp[2] = {pp0[0], pp0[1]};
+    if constexpr (DROP) {
+      // Elements 8 h + 2 e and 8 h + 2 e + 1: bytes 2 (e % 2) and
+      // 2 (e % 2) + 1 of flag word 2 h + e / 2.
+      const u32x4 kf = kex[(pair * 2 + qb) * 64 + lane];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pp[h][e] &= keep_mask_pair(kf[2 * h + (e >> 1)], e & 1);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -420,8 +427,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   };
 
   // Role B, phase 2: dS = P (dP - delta), dK^T += Q^T dS.
-  auto phase_b2 = [&] __device__ (const char* qt, const float* st, int qb, const f32x16& dp)
-      __attribute__((always_inline)) {
+  auto phase_b2 = [&] __device__ (const char* qt, const float* st, int qb, const f32x16& dp,
+                                  const u32x4& kf) __attribute__((always_inline)) {
     const f32x4* src = pex + ((pair * 2 + qb) * 4) * 64 + lane;
     float ds[16];
 #pragma unroll
@@ -431,15 +438,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (DROP) {
-          // dS = P (keep * dP / (1 - p) - delta), the keep bit in P's sign
-          // (a dropped P of 0 reads as kept, which changes nothing since
-          // its dS is 0). Float operations on the element: this compiler
-          // evaluates __builtin_bit_cast of a vector element (p4[e]) as a
-          // bit_cast of element 0, which is what made an integer decode of
-          // the sign wrong.
-          const float pv = fabsf(p4[e]);
-          const float g = p4[e] < 0.f ? 0.f : dp[4 * m + e] * drop.inv_keep;
-          ds[4 * m + e] = pv * (g - d4[e]);
+          // dS = P (keep * dP / (1 - p) - delta): the scaled dP, its bits
+          // cleared where dropped.
+          const float t = dp[4 * m + e] * drop.inv_keep;
+          const float g = __uint_as_float(__float_as_uint(t) & keep_mask_elem(kf[m], e));
+          ds[4 * m + e] = p4[e] * (g - d4[e]);
         } else {
           ds[4 * m + e] = p4[e] * (dp[4 * m + e] - d4[e]);
         }
@@ -476,11 +479,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
       phase_a2(gt, 1, pp[1]);
     } else {
       f32x16 dp[2];
-      phase_b1(gt, 0, dp[0]);
-      phase_b1(gt, 1, dp[1]);
+      u32x4 kf[2] = {};
+      const int i = DROP ? item_tile(u) : 0, h = DROP ? item_head(u) : 0;
+      phase_b1(gt, 0, dp[0], i, h, kf[0]);
+      phase_b1(gt, 1, dp[1], i, h, kf[1]);
       __syncthreads();
-      phase_b2(qt, st, 0, dp[0]);
-      phase_b2(qt, st, 1, dp[1]);
+      phase_b2(qt, st, 0, dp[0], kf[0]);
+      phase_b2(qt, st, 1, dp[1], kf[1]);
     }
   };
 
@@ -645,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
     // (the whole training backward 0.2-0.8 % faster than with them fenced
     // apart, in interleaved runs on two boxes); with dropout fenced, so that
     // one set of operand fragments
-    // is live at a time (unfenced, the keep bits' registers push it into
+    // is live at a time (unfenced, the keep bytes' registers push it into
     // spills).
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s = TT::mma(rd_row<D>(kt, 32 * half, ldo, kk), qf[kk], s);
@@ -654,8 +659,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
     for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(vt, 32 * half, ldo, kk), gf[kk], dp);
     if constexpr (DROP) __builtin_amdgcn_sched_barrier(0);
     float ds[16];
-    uint32_t kept = 0xffffu;
-    if constexpr (DROP) kept = keep_bits_rows(drop, bh, qi, 32 * b, hi, lane & 3);
+    u32x4 kb = {};
+    if constexpr (DROP) kb = keep_bytes_rows(drop, bh, qi, 32 * b, hi, lane & 3);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = fast_exp2(fmaf(s[r], c, -l2));
@@ -666,7 +671,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
       }
       if constexpr (DROP) {
         // dS = P (keep * dP / (1 - p) - delta)
-        ds[r] = p * ((((kept >> r) & 1u) ? dp[r] * drop.inv_keep : 0.f) - dl);
+        ds[r] = p * ((byte_kept(kb, r, drop.thr) ? dp[r] * drop.inv_keep : 0.f) - dl);
       } else {
         ds[r] = p * (dp[r] - dl);
       }

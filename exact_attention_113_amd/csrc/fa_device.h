@@ -161,28 +161,18 @@ __device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], flo
 // key; each round multiplies counter words 0 and 2 by two fixed constants,
 // crosses the high halves into words 1 and 3 with the key, and the key is
 // bumped by two Weyl constants.
-// WIDE forms each 32 x 32 -> 64-bit product with one multiply that gives
-// both halves (one instruction instead of two, but a register pair; the
-// same bits either way).
-template <bool WIDE = false>
+// Each 32 x 32 -> 64-bit product is one multiply that gives both halves
+// (v_mad_u64_u32), not a low and a high multiply.
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    uint32_t hi0, lo0, hi1, lo1;
-    if constexpr (WIDE) {
-      const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-      const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-      hi0 = (uint32_t)(p0 >> 32);
-      lo0 = (uint32_t)p0;
-      hi1 = (uint32_t)(p1 >> 32);
-      lo1 = (uint32_t)p1;
-    } else {
-      hi0 = __umulhi(0xD2511F53u, c[0]);
-      lo0 = 0xD2511F53u * c[0];
-      hi1 = __umulhi(0xCD9E8D57u, c[2]);
-      lo1 = 0xCD9E8D57u * c[2];
-    }
-    c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    // Three-input XOR (bitop3 truth table 0x96): one instruction, not two.
+    c = u32x4{(uint32_t)__builtin_amdgcn_bitop3_b32(hi1, c[1], k0, 0x96), lo1,
+              (uint32_t)__builtin_amdgcn_bitop3_b32(hi0, c[3], k1, 0x96), lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -227,47 +217,95 @@ __device__ __forceinline__ u32x4 quad_transpose(u32x4 x, int s) {
 }
 
 // 4x4 transpose of the bytes of four words: byte t of word w becomes byte w
-// of word t.
+// of word t. Two rounds of byte selects (v_perm: selector bytes 0 .. 3 pick
+// from the second source, 4 .. 7 from the first): first the words pair up
+// into (w0, w1) and (w2, w3) interleaves, then the interleaves into rows.
 __device__ __forceinline__ u32x4 byte_transpose(u32x4 x) {
-  u32x4 out;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    out[t] = ((x[0] >> (8 * t)) & 0xffu) | (((x[1] >> (8 * t)) & 0xffu) << 8) |
-             (((x[2] >> (8 * t)) & 0xffu) << 16) | (((x[3] >> (8 * t)) & 0xffu) << 24);
-  return out;
+  const uint32_t a = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+  const uint32_t b = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+  const uint32_t c = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t d = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  return u32x4{(uint32_t)__builtin_amdgcn_perm(c, a, 0x05040100u),
+               (uint32_t)__builtin_amdgcn_perm(c, a, 0x07060302u),
+               (uint32_t)__builtin_amdgcn_perm(d, b, 0x05040100u),
+               (uint32_t)__builtin_amdgcn_perm(d, b, 0x07060302u)};
 }
 
-// Keep bits of the 16 scores a lane holds in the transposed-score layout
-// (lane = one row, register r = key 8 (r / 4) + 4 hi + r % 4 of a 32-key
-// block starting at key0; the four lanes of a quad hold rows 4a .. 4a + 3).
-// Bit r of the result is set when element r is kept. Each lane of the quad
-// computes one of the four calls its rows need.
-template <bool WIDE = false>
-__device__ __forceinline__ uint32_t keep_bits_rows(const DropParams& dp, int bh, int row,
-                                                   int key0, int hi, int s) {
-  const u32x4 w = philox4x32_10<WIDE>(
+// Keep flags of four bytes at once: bit 7 of byte k of the result is set
+// when byte k of x, read as an unsigned number, is at least thr (0 <= thr <=
+// 255; thr4 = thr in every byte, c4 = 0x80808080 - (thr4 & 0x7f7f7f7f), both
+// precomputed on the host); the other bits are undefined. (x & 0x7f7f7f7f) + c4 carries into no other
+// byte, and its bit 7 in byte k says whether the low seven bits of x reach
+// those of thr there; where the top bits of x and thr differ, they decide.
+// Both together: the top bit of the majority of x, NOT thr4 and that sum
+// (bitop3 truth table 0xB2).
+__device__ __forceinline__ uint32_t keep_flags4(uint32_t x, uint32_t thr4, uint32_t c4) {
+  return (uint32_t)__builtin_amdgcn_bitop3_b32(x, thr4, (x & 0x7f7f7f7fu) + c4, 0xB2);
+}
+
+// From a word of keep flags g: 0xffff in the low half when the element of
+// byte 2q is kept, and in the high half when that of byte 2q + 1 is. v_perm
+// selectors 8 .. 11 copy bit 15 or bit 31 of either source into a whole
+// byte: g holds the flags of bytes 1 and 3 there, g << 8 those of 0 and 2.
+__device__ __forceinline__ uint32_t keep_mask_pair(uint32_t g, int q) {
+  return (uint32_t)__builtin_amdgcn_perm(g << 8, g, q ? 0x09090b0bu : 0x08080a0au);
+}
+
+// The random bytes of the 16 scores a lane holds in the transposed-score
+// layout (lane = one row, register r = key 8 (r / 4) + 4 hi + r % 4 of a
+// 32-key block starting at key0; the four lanes of a quad hold rows 4a ..
+// 4a + 3): byte r % 4 of word r / 4 belongs to element r, which is kept when
+// that byte is at least thr. Each lane of the quad computes one of the four
+// calls its rows need.
+__device__ __forceinline__ u32x4 keep_bytes_rows(const DropParams& dp, int bh, int row,
+                                                 int key0, int hi, int s) {
+  const u32x4 w = philox4x32_10(
       u32x4{(uint32_t)((key0 >> 2) + 2 * s + hi), (uint32_t)(row >> 2), (uint32_t)bh, dp.offset},
       dp.k0, dp.k1);
-  const u32x4 v = quad_transpose(w, s);  // v[m] = word (row % 4) of call m
-  uint32_t bits = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) bits |= (((v[r >> 2] >> (8 * (r & 3))) & 0xffu) >= dp.thr ? 1u : 0u) << r;
-  return bits;
+  return quad_transpose(w, s);  // word m = word (row % 4) of call m
 }
 
 // The same for the layout with rows in the registers: lane = one key,
 // register r = row 8 (r / 4) + 4 hi + r % 4 of a 32-row block starting at
 // row0; the four lanes of a quad hold keys 4b .. 4b + 3.
-__device__ __forceinline__ uint32_t keep_bits_keys(const DropParams& dp, int bh, int key,
-                                                   int row0, int hi, int s) {
+__device__ __forceinline__ u32x4 keep_bytes_keys(const DropParams& dp, int bh, int key,
+                                                 int row0, int hi, int s) {
   const u32x4 w = philox4x32_10(
       u32x4{(uint32_t)(key >> 2), (uint32_t)((row0 >> 2) + 2 * s + hi), (uint32_t)bh, dp.offset},
       dp.k0, dp.k1);
-  const u32x4 v = quad_transpose(byte_transpose(w), s);  // v[m] byte e: row 4 m' + e, this key
-  uint32_t bits = 0;
+  return quad_transpose(byte_transpose(w), s);  // word m byte e: row 4 m' + e, this key
+}
+
+// Whether element r of a keep_bytes_* result is kept.
+__device__ __forceinline__ bool byte_kept(const u32x4& v, int r, uint32_t thr) {
+  return ((v[r >> 2] >> (8 * (r & 3))) & 0xffu) >= thr;
+}
+
+// 0xffffffff when the element of byte k (a compile-time 0 .. 3) of flag word
+// g is kept, else 0 (keep_mask_pair's selectors, one byte's flag in all four).
+__device__ __forceinline__ uint32_t keep_mask_elem(uint32_t g, int k) {
+  const uint32_t sel = k == 0 ? 0x0a0a0a0au : k == 1 ? 0x08080808u : k == 2 ? 0x0b0b0b0bu : 0x09090909u;
+  return (uint32_t)__builtin_amdgcn_perm(g << 8, g, sel);
+}
+
+// keep_bytes_keys as keep flags (keep_flags4 on each word).
+__device__ __forceinline__ u32x4 keep_flags_keys(const DropParams& dp, int bh, int key,
+                                                 int row0, int hi, int s) {
+  const u32x4 v = keep_bytes_keys(dp, bh, key, row0, hi, s);
+  u32x4 g;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) bits |= (((v[r >> 2] >> (8 * (r & 3))) & 0xffu) >= dp.thr ? 1u : 0u) << r;
-  return bits;
+  for (int m = 0; m < 4; ++m) g[m] = keep_flags4(v[m], dp.thr4, dp.bias4);
+  return g;
+}
+
+// keep_bytes_rows as keep flags (keep_flags4 on each word).
+__device__ __forceinline__ u32x4 keep_flags_rows(const DropParams& dp, int bh, int row,
+                                                 int key0, int hi, int s) {
+  const u32x4 v = keep_bytes_rows(dp, bh, row, key0, hi, s);
+  u32x4 g;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) g[m] = keep_flags4(v[m], dp.thr4, dp.bias4);
+  return g;
 }
 
 }  // namespace fa

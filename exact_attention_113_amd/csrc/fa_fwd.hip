@@ -317,14 +317,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   // 1 / (1 - p) at the end.
   auto drop_operand = [&](int b, const float (&p)[16], u32x4 (&pf)[2])
       __attribute__((always_inline)) {
-    const uint32_t bits = keep_bits_rows<true>(prm.drop, bh, qi, kKB * b, hi, lane & 3);
+    // Elements 8 h + 2 e and 8 h + 2 e + 1 are bytes 2 (e % 2) and
+    // 2 (e % 2) + 1 of flag word 2 h + e / 2; a dropped one's half is cleared.
+    const u32x4 g = keep_flags_rows(prm.drop, bh, qi, kKB * b, hi, lane & 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * h + 2 * e;
-        pf[h][e] = TT::pack2(((bits >> r) & 1u) ? p[r] : 0.f,
-                             ((bits >> (r + 1)) & 1u) ? p[r + 1] : 0.f);
+        pf[h][e] = TT::pack2(p[r], p[r + 1]) & keep_mask_pair(g[2 * h + (e >> 1)], e & 1);
       }
   };
 

@@ -17,6 +17,8 @@ struct DropParams {
   uint32_t k0, k1;    // seed, low and high 32 bits
   uint32_t offset;
   float inv_keep;     // 1 / (1 - thr / 256)
+  uint32_t thr4;      // thr in each of the four bytes
+  uint32_t bias4;     // 0x80808080 - (thr4 & 0x7f7f7f7f): see keep_flags4
 };
 
 struct FwdArgs {
