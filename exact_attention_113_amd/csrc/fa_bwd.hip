@@ -250,6 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
   // With dropout, the keep flags of each pair's scores (role B computes
   // them, role A masks its dV operand with them): [pair][q-block][64 lanes].
   __shared__ __attribute__((aligned(16))) u32x4 kex[DROP ? 4 * 2 * 64 : 1];
+  // With dropout: each role-B wave's area for the keep bytes' quad transpose.
+  __shared__ __attribute__((aligned(16))) uint32_t dxa[DROP ? 4 * kQuadXWords : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -402,7 +404,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const BwdParams p
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) dp = TT::mma(rd_row<D>(gt, 32 * qb, ldo, kk), bf[kk], dp);
     if constexpr (DROP) {
-      kf = keep_flags_keys(drop, bidx * prm.heads + h, key, i * BM + 32 * qb, hi, lane & 3);
+      kf = keep_flags_keys(drop, bidx * prm.heads + h, key, i * BM + 32 * qb, hi, lane,
+                           dxa + pair * kQuadXWords);
       kex[(pair * 2 + qb) * 64 + lane] = kf;
     }
   };
@@ -549,6 +552,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
   __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
   __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
+  // With dropout: each wave's area for the keep bytes' quad transpose.
+  __shared__ __attribute__((aligned(16))) uint32_t dxa[DROP ? kWaves * kQuadXWords : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -660,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const BwdParams prm
     if constexpr (DROP) __builtin_amdgcn_sched_barrier(0);
     float ds[16];
     u32x4 kb = {};
-    if constexpr (DROP) kb = keep_bytes_rows(drop, bh, qi, 32 * b, hi, lane & 3);
+    if constexpr (DROP) kb = keep_bytes_rows(drop, bh, qi, 32 * b, hi, lane, dxa + w * kQuadXWords);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = fast_exp2(fmaf(s[r], c, -l2));

@@ -184,36 +184,21 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 // is below thr (thr = floor(256 p + 0.5)).
 // (DropParams, the per-call constants, is declared in fa_internal.h.)
 
-__device__ __forceinline__ uint32_t quad_xor1(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-}
-__device__ __forceinline__ uint32_t quad_xor2(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
-}
-
 // 4x4 transpose of 32-bit words across the four lanes of a quad: lane s
-// holds row s (x[0..3]) on entry and column s (x[0..3] = rows 0..3 of
-// column s) on return. Two exchanges (lanes s ^ 2, then s ^ 1).
-__device__ __forceinline__ u32x4 quad_transpose(u32x4 x, int s) {
-  const bool b1 = (s & 2) != 0, b0 = (s & 1) != 0;
-  // Stage 1: keep the two columns c with c & 2 == s & 2, swap the others.
-  const uint32_t r0 = quad_xor2(b1 ? x[0] : x[2]);
-  const uint32_t r1 = quad_xor2(b1 ? x[1] : x[3]);
-  const uint32_t own0 = b1 ? x[2] : x[0], own1 = b1 ? x[3] : x[1];  // row s, cols (s&2)+0,1
-  // (r0, r1): row s ^ 2, the same two columns.
-  // Stage 2: keep column s, swap the other one of the pair.
-  const uint32_t q0 = quad_xor1(b0 ? own0 : own1);  // row s ^ 1, column s
-  const uint32_t q1 = quad_xor1(b0 ? r0 : r1);      // row s ^ 3, column s
-  const uint32_t mine = b0 ? own1 : own0;           // row s, column s
-  const uint32_t par = b0 ? r1 : r0;                // row s ^ 2, column s
-  // Rows in order: row k is at relative position k ^ s.
-  u32x4 out;
+// holds row s (x[0..3]) on entry and column s (rows 0..3 of column s) on
+// return. It goes through LDS, one wave's own area of kQuadXWords words
+// (16-byte aligned): word e of lane L is stored at word 80 e + L, and lane
+// 4 q + s reads words 80 s + 4 q .. 80 s + 4 q + 3, word s of its quad's four
+// lanes (three LDS instructions; the same with DPP lane exchanges took about
+// twenty vector instructions). A wave's LDS accesses complete in order, so
+// the area needs no barrier between uses; rows 80 words apart keep the word
+// stores and the 16-byte reads free of bank conflicts.
+constexpr int kQuadXWords = 3 * 80 + 64;
+__device__ __forceinline__ u32x4 quad_transpose_lds(u32x4 x, uint32_t* area, int lane) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int rel = k ^ s;
-    out[k] = rel == 0 ? mine : rel == 1 ? q0 : rel == 2 ? par : q1;
-  }
-  return out;
+  for (int e = 0; e < 4; ++e) area[80 * e + lane] = x[e];
+  __builtin_amdgcn_wave_barrier();
+  return *(const u32x4*)(area + 80 * (lane & 3) + 4 * (lane >> 2));
 }
 
 // 4x4 transpose of the bytes of four words: byte t of word w becomes byte w
@@ -256,24 +241,27 @@ __device__ __forceinline__ uint32_t keep_mask_pair(uint32_t g, int q) {
 // 32-key block starting at key0; the four lanes of a quad hold rows 4a ..
 // 4a + 3): byte r % 4 of word r / 4 belongs to element r, which is kept when
 // that byte is at least thr. Each lane of the quad computes one of the four
-// calls its rows need.
+// calls its rows need, and the quad transposes them through xa, the wave's
+// kQuadXWords-word LDS area.
 __device__ __forceinline__ u32x4 keep_bytes_rows(const DropParams& dp, int bh, int row,
-                                                 int key0, int hi, int s) {
+                                                 int key0, int hi, int lane, uint32_t* xa) {
+  const int s = lane & 3;
   const u32x4 w = philox4x32_10(
       u32x4{(uint32_t)((key0 >> 2) + 2 * s + hi), (uint32_t)(row >> 2), (uint32_t)bh, dp.offset},
       dp.k0, dp.k1);
-  return quad_transpose(w, s);  // word m = word (row % 4) of call m
+  return quad_transpose_lds(w, xa, lane);  // word m = word (row % 4) of call m
 }
 
 // The same for the layout with rows in the registers: lane = one key,
 // register r = row 8 (r / 4) + 4 hi + r % 4 of a 32-row block starting at
 // row0; the four lanes of a quad hold keys 4b .. 4b + 3.
 __device__ __forceinline__ u32x4 keep_bytes_keys(const DropParams& dp, int bh, int key,
-                                                 int row0, int hi, int s) {
+                                                 int row0, int hi, int lane, uint32_t* xa) {
+  const int s = lane & 3;
   const u32x4 w = philox4x32_10(
       u32x4{(uint32_t)(key >> 2), (uint32_t)((row0 >> 2) + 2 * s + hi), (uint32_t)bh, dp.offset},
       dp.k0, dp.k1);
-  return quad_transpose(byte_transpose(w), s);  // word m byte e: row 4 m' + e, this key
+  return quad_transpose_lds(byte_transpose(w), xa, lane);  // word m byte e: row 4 m' + e, this key
 }
 
 // Whether element r of a keep_bytes_* result is kept.
@@ -290,8 +278,8 @@ __device__ __forceinline__ uint32_t keep_mask_elem(uint32_t g, int k) {
 
 // keep_bytes_keys as keep flags (keep_flags4 on each word).
 __device__ __forceinline__ u32x4 keep_flags_keys(const DropParams& dp, int bh, int key,
-                                                 int row0, int hi, int s) {
-  const u32x4 v = keep_bytes_keys(dp, bh, key, row0, hi, s);
+                                                 int row0, int hi, int lane, uint32_t* xa) {
+  const u32x4 v = keep_bytes_keys(dp, bh, key, row0, hi, lane, xa);
   u32x4 g;
 #pragma unroll
   for (int m = 0; m < 4; ++m) g[m] = keep_flags4(v[m], dp.thr4, dp.bias4);
@@ -300,8 +288,8 @@ __device__ __forceinline__ u32x4 keep_flags_keys(const DropParams& dp, int bh, i
 
 // keep_bytes_rows as keep flags (keep_flags4 on each word).
 __device__ __forceinline__ u32x4 keep_flags_rows(const DropParams& dp, int bh, int row,
-                                                 int key0, int hi, int s) {
-  const u32x4 v = keep_bytes_rows(dp, bh, row, key0, hi, s);
+                                                 int key0, int hi, int lane, uint32_t* xa) {
+  const u32x4 v = keep_bytes_rows(dp, bh, row, key0, hi, lane, xa);
   u32x4 g;
 #pragma unroll
   for (int m = 0; m < 4; ++m) g[m] = keep_flags4(v[m], dp.thr4, dp.bias4);

@@ -150,6 +150,8 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
   // first of its row group.
   constexpr int NX = KS > 1 ? NRG * (KS - 1) : 1;
   __shared__ float xm[NX][64], xl[NX][64];
+  // With dropout: each wave's area for the keep bytes' quad transpose.
+  __shared__ __attribute__((aligned(16))) uint32_t dxa[DROP ? NW * kQuadXWords : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const FwdParams prm) {
       __attribute__((always_inline)) {
     // Elements 8 h + 2 e and 8 h + 2 e + 1 are bytes 2 (e % 2) and
     // 2 (e % 2) + 1 of flag word 2 h + e / 2; a dropped one's half is cleared.
-    const u32x4 g = keep_flags_rows(prm.drop, bh, qi, kKB * b, hi, lane & 3);
+    const u32x4 g = keep_flags_rows(prm.drop, bh, qi, kKB * b, hi, lane, dxa + w * kQuadXWords);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
