@@ -39,6 +39,7 @@ PROTOTYPES = {
     "fa_backward_varlen_dropout": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                                   _I64, _I64, _I64, _I64, _I64, _I64, _F, _I, _I,
                                                   _F, _U64, _U64, _P]),
+    "fa_clock_probe": (ctypes.c_int, [_P, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
 }

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_decode.hip",
+           "fa_clock.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -558,3 +558,11 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
                    scale, dtype, (hipStream_t)stream};
   return hip_status(fa::launch_decode(a, plan), "fa_decode");
 }
+
+fa_status fa_clock_probe(uint64_t* out, int iters, void* stream) {
+  g_last_error[0] = '\0';
+  if (!out) return fail(FA_ERR_INVALID_ARGUMENT, "fa_clock_probe: out must be non-NULL");
+  if (misaligned(out, 8)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_clock_probe: out must be 8-byte aligned");
+  if (iters < 1) return fail(FA_ERR_INVALID_ARGUMENT, "fa_clock_probe: iters must be >= 1 (got %d)", iters);
+  return hip_status(fa::launch_clock_probe(out, iters, (hipStream_t)stream), "fa_clock_probe");
+}

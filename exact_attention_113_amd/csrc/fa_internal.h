@@ -94,5 +94,6 @@ hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a, const BwdWorkspace& ws);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan);
+hipError_t launch_clock_probe(uint64_t* out, int iters, hipStream_t stream);
 
 }  // namespace fa

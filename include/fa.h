@@ -417,6 +417,26 @@ fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const
                               int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
                               int dtype, void* stream);
 
+/*
+ * fa_clock_probe - a measurement aid, not part of the attention path: the
+ * shader clock the GPU runs at while other work occupies it, so that a
+ * throughput can be set against the peak at the clock actually held. One
+ * wave of one workgroup (no LDS) spins through `iters` dependent fused
+ * multiply-adds between two reads of the shader cycle counter and of the
+ * 100 MHz constant clock, and stores the deltas:
+ *   out[0]  shader cycles over the spin
+ *   out[1]  constant-clock ticks (10 ns each) over the spin
+ *   out[2]  unspecified (keeps the spin from being optimised away)
+ * The clock in MHz is out[0] / out[1] * 100. Launch it on a stream of its
+ * own beside the work to be measured; 10^5 iterations take about 1.5 ms.
+ *   out     device, 3 x uint64, 8-byte aligned; written by the kernel
+ *   iters   >= 1
+ *   stream  HIP stream (NULL: the default stream); asynchronous
+ * Returns FA_ERR_INVALID_ARGUMENT (NULL or misaligned out, iters < 1) before
+ * any HIP call, FA_ERR_HIP if the launch fails, else FA_OK.
+ */
+fa_status fa_clock_probe(uint64_t* out, int iters, void* stream);
+
 /* fa_status_string - static, never-NULL name of a status code. */
 const char* fa_status_string(int status);
 

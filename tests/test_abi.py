@@ -35,6 +35,14 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_clock_probe_rejects_bad_arguments():
+    lib = _lib.load()
+    assert lib.fa_clock_probe(None, 1000, None) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_clock_probe(A + 4, 1000, None) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_clock_probe(A, 0, None) == _lib.FA_ERR_INVALID_ARGUMENT
+    assert "iters" in _lib.last_error()
+
+
 def test_status_strings():
     names = ["FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
              "FA_ERR_HIP"]
