@@ -12,8 +12,10 @@ byte. Both steps are checked here, exhaustively over bytes and thresholds,
 against the plain comparison; the v_perm model follows the instruction's
 published definition (selector bytes 0 .. 3 pick bytes of the second source,
 4 .. 7 of the first, 8 .. 11 sign-extend bits 15 and 31 of the second and of
-the first, 12 gives 0x00). The GPU parity tests check the same masks on the
-device, bit for bit against the oracle's keep decisions."""
+the first, 12 gives 0x00). The byte transpose's selectors and the LDS
+layout of the quad transpose are checked the same way (the transpose, the
+area's bounds, alignment and banks). The GPU parity tests check the same
+masks on the device, bit for bit against the oracle's keep decisions."""
 
 import numpy as np
 
@@ -101,3 +103,54 @@ def test_mutant_without_top_bit_term_fails():
     t4 = thr * 0x01010101
     d = (x & np.uint32(M7)) + np.uint32(0x80808080 - (t4 & M7))
     assert not np.array_equal((d >> 7) & 1, (x >= thr).astype(np.uint32))
+
+
+# The quad transpose of the Philox words goes through a per-wave LDS area:
+# lane L stores its word e at word 80 e + L, lane 4 q + s reads the four
+# words from 80 s + 4 q. The layout constants are restated here from the
+# kernel source and checked for the transpose, the bounds of the area
+# (kQuadXWords words), the 16-byte alignment of the reads, and bank
+# conflicts (64 banks of 4 bytes; 16-byte reads served 16 lanes at a time).
+QUAD_X_WORDS = 3 * 80 + 64
+
+
+def test_quad_transpose_layout():
+    area = {}
+    for lane in range(64):
+        for e in range(4):
+            addr = 80 * e + lane
+            assert 0 <= addr < QUAD_X_WORDS
+            assert addr not in area
+            area[addr] = (lane, e)  # word e of lane `lane`
+    for lane in range(64):
+        q, s = lane >> 2, lane & 3
+        base = 80 * s + 4 * q
+        assert base % 4 == 0 and base + 3 < QUAD_X_WORDS  # 16-byte aligned, in bounds
+        got = [area[base + m] for m in range(4)]
+        # column s of the quad: word s of lanes 4q + 0 .. 4q + 3, in order
+        assert got == [(4 * q + m, s) for m in range(4)]
+    for e in range(4):  # each store instruction: 64 lanes, distinct banks
+        assert len({(80 * e + lane) % 64 for lane in range(64)}) == 64
+    for first in range(0, 64, 16):  # each 16-lane phase of the 16-byte read
+        banks = [(80 * (l & 3) + 4 * (l >> 2) + m) % 64 for l in range(first, first + 16)
+                 for m in range(4)]
+        assert len(set(banks)) == 64
+
+
+def byte_transpose(x):
+    a = v_perm(x[1], x[0], 0x05010400)
+    b = v_perm(x[1], x[0], 0x07030602)
+    c = v_perm(x[3], x[2], 0x05010400)
+    d = v_perm(x[3], x[2], 0x07030602)
+    return [v_perm(c, a, 0x05040100), v_perm(c, a, 0x07060302),
+            v_perm(d, b, 0x05040100), v_perm(d, b, 0x07060302)]
+
+
+def test_byte_transpose_selectors():
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        x = [int(v) for v in rng.integers(0, 2 ** 32, size=4)]
+        out = byte_transpose(x)
+        for t in range(4):
+            for w in range(4):
+                assert (out[t] >> (8 * w)) & 0xFF == (x[w] >> (8 * t)) & 0xFF
